@@ -1,0 +1,199 @@
+"""Python binding of libsegattn.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Device buffers are
+torch tensors (torch provides device memory and the current HIP stream);
+item tables are host ``numpy.int64`` arrays of shape [n, 5] with columns
+(seq_off, q_lo, q_hi, k_lo, k_hi).  A nonzero status raises ``SegattnError``
+carrying ``segattn_last_error()``.  Nothing here computes any part of the
+attention path: all of it runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (SEGATTN_ACCUMULATE, SEGATTN_BF16, SEGATTN_D_READY, SEGATTN_F32,  # noqa: F401
+                   SEGATTN_MERGE_INTO, Item, SegattnError, Shape, check, lib)
+
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_ITEMP = ctypes.POINTER(Item)
+
+_DTYPE_CODE = {torch.bfloat16: SEGATTN_BF16, torch.float32: SEGATTN_F32}
+_CODE_DTYPE = {SEGATTN_BF16: torch.bfloat16, SEGATTN_F32: torch.float32}
+
+
+# ------------------------------------------------------------------ helpers
+
+def _items_arg(items):
+    a = np.ascontiguousarray(np.asarray(items, dtype=np.int64).reshape(-1, 5))
+    return a, a.ctypes.data_as(_ITEMP), a.shape[0]
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_shape(q, k, scale=None):
+    """segattn_shape for token-major q [T, hq, d] and k [T, hkv, d]."""
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [T, hq, d] and k [T, hkv, d]")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype:
+        raise TypeError("q, k, v must all be bfloat16 or all float32")
+    d = q.shape[2]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return Shape(q.shape[0], q.shape[1], k.shape[1], d, _DTYPE_CODE[q.dtype], sc)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {nbytes} bytes needed")
+    return workspace
+
+
+# ------------------------------------------------------------------ planner
+
+def segattn_partition(S, N):
+    out = np.zeros(int(N) + 1 if int(N) >= 0 else 1, dtype=np.int64)
+    check(lib().segattn_partition(int(S), int(N), out.ctypes.data_as(_I64P)))
+    return out
+
+
+def segattn_partition_varlen(cu_seqlens, max_slice):
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = ctypes.c_int32(0)
+    L = lib()
+    st = L.segattn_partition_varlen(cu.ctypes.data_as(_I64P), len(cu) - 1, int(max_slice), None, 0,
+                                    ctypes.byref(n))
+    if st != _lib.SEGATTN_E_CAPACITY:
+        check(st)
+        if n.value == 0:
+            return np.zeros((0, 5), dtype=np.int64)
+    out = np.zeros((n.value, 5), dtype=np.int64)
+    check(L.segattn_partition_varlen(cu.ctypes.data_as(_I64P), len(cu) - 1, int(max_slice),
+                                     out.ctypes.data_as(_ITEMP), n.value, ctypes.byref(n)))
+    return out
+
+
+def segattn_ring_items(bounds, block):
+    b = np.ascontiguousarray(np.asarray(bounds, dtype=np.int64))
+    n = ctypes.c_int32(0)
+    L = lib()
+    st = L.segattn_ring_items(b.ctypes.data_as(_I64P), len(b) - 1, int(block), None, 0, ctypes.byref(n))
+    if st != _lib.SEGATTN_E_CAPACITY:
+        check(st)
+    out = np.zeros((n.value, 5), dtype=np.int64)
+    check(L.segattn_ring_items(b.ctypes.data_as(_I64P), len(b) - 1, int(block), out.ctypes.data_as(_ITEMP),
+                               n.value, ctypes.byref(n)))
+    return out
+
+
+# ------------------------------------------------------------------ forward
+
+def segattn_fwd_workspace(shape, items):
+    arr, p, n = _items_arg(items)
+    nb = ctypes.c_size_t(0)
+    check(lib().segattn_fwd_workspace(ctypes.byref(shape), p, n, ctypes.byref(nb)))
+    return nb.value
+
+
+def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, merge_into=False,
+                workspace=None, stream=None):
+    """Partial attention of `items` into (o, lse); returns (o, lse).
+    New outputs are allocated (o_dtype defaults to q's dtype; lse filled
+    with -inf) when not given."""
+    shape = make_shape(q, k, scale)
+    arr, p, n = _items_arg(items)
+    if o is None:
+        od = _CODE_DTYPE[o_dtype] if isinstance(o_dtype, int) else (o_dtype or q.dtype)
+        o = torch.zeros((q.shape[0], q.shape[1], q.shape[2]), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.full((q.shape[1], q.shape[0]), -math.inf, dtype=torch.float32, device=q.device)
+    ocode = _DTYPE_CODE[o.dtype]
+    ws = _workspace(segattn_fwd_workspace(shape, arr), q.device, workspace)
+    flags = SEGATTN_MERGE_INTO if merge_into else 0
+    check(lib().segattn_fwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), p, n,
+                            _dev(o, "o"), ocode, _dev(lse, "lse", torch.float32), flags,
+                            _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+    return o, lse
+
+
+def segattn_merge(o_a, lse_a, o_b, lse_b, *, o_out=None, lse_out=None, rows=None, lse_stride=None,
+                  stream=None):
+    """Log-sum-exp merge of fp32 partials o [rows, h, d], lse [h, >= rows]."""
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    r = o_a.shape[0] if rows is None else int(rows)
+    stride = lse_a.shape[-1] if lse_stride is None else int(lse_stride)
+    for t, nm in ((o_a, "o_a"), (o_b, "o_b"), (o_out, "o_out")):
+        _dev(t, nm, torch.float32)
+    for t, nm in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse_out, "lse_out")):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{nm} must be a float32 device tensor")
+    check(lib().segattn_merge(r, o_a.shape[1], o_a.shape[2], stride, ctypes.c_void_p(o_a.data_ptr()),
+                              ctypes.c_void_p(lse_a.data_ptr()), ctypes.c_void_p(o_b.data_ptr()),
+                              ctypes.c_void_p(lse_b.data_ptr()), ctypes.c_void_p(o_out.data_ptr()),
+                              ctypes.c_void_p(lse_out.data_ptr()), _stream(stream)))
+    return o_out, lse_out
+
+
+# ----------------------------------------------------------------- backward
+
+def segattn_bwd_workspace(shape, items):
+    arr, p, n = _items_arg(items)
+    nb = ctypes.c_size_t(0)
+    check(lib().segattn_bwd_workspace(ctypes.byref(shape), p, n, ctypes.byref(nb)))
+    return nb.value
+
+
+def segattn_bwd_preprocess(q, k, o, do, items, workspace, *, scale=None, stream=None):
+    shape = make_shape(q, k, scale)
+    arr, p, n = _items_arg(items)
+    check(lib().segattn_bwd_preprocess(ctypes.byref(shape), _dev(o, "o"), _DTYPE_CODE[o.dtype], _dev(do, "do"),
+                                       p, n, _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def segattn_bwd(q, k, v, o, lse, do, items, *, scale=None, dq=None, dk=None, dv=None, g_dtype=None,
+                accumulate=False, d_ready=False, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(do * o); allocated (zero-filled) when
+    not given, in g_dtype (default q's dtype; float32 with accumulate)."""
+    shape = make_shape(q, k, scale)
+    arr, p, n = _items_arg(items)
+    gd = g_dtype or (torch.float32 if accumulate else q.dtype)
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=gd, device=q.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=gd, device=q.device)
+    if dv is None:
+        dv = torch.zeros(v.shape, dtype=gd, device=q.device)
+    ws = _workspace(segattn_bwd_workspace(shape, arr), q.device, workspace)
+    flags = (SEGATTN_ACCUMULATE if accumulate else 0) | (SEGATTN_D_READY if d_ready else 0)
+    check(lib().segattn_bwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                            _DTYPE_CODE[o.dtype], _dev(lse, "lse", torch.float32), _dev(do, "do"), p, n,
+                            _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _DTYPE_CODE[dq.dtype], flags,
+                            _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def segattn_version():
+    return lib().segattn_version().decode()

@@ -1,0 +1,418 @@
+// C-ABI entry points of the attention path: argument validation (all of it
+// on the host, before anything is launched), work-table construction, the
+// table upload into the caller's workspace, and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "segattn.h"
+#include "status.h"
+
+using namespace segattn;
+
+namespace {
+
+constexpr int64_t kMaxTokens = 0x7fffffffLL;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void *p, const char *fn, const char *name) {
+  if (!p) return fail(SEGATTN_E_INVALID, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(SEGATTN_E_INVALID, "%s: %s is not 16-byte aligned", fn, name);
+  return SEGATTN_OK;
+}
+
+int check_shape(const segattn_shape *s, const char *fn) {
+  if (!s) return fail(SEGATTN_E_INVALID, "%s: shape is NULL", fn);
+  if (s->tokens < 1 || s->tokens > kMaxTokens)
+    return fail(SEGATTN_E_RANGE, "%s: tokens = %lld outside [1, 2^31-1]", fn, (long long)s->tokens);
+  if (s->hq < 1 || s->hkv < 1) return fail(SEGATTN_E_INVALID, "%s: hq, hkv must be >= 1", fn);
+  if (s->hq % s->hkv) return fail(SEGATTN_E_UNSUPPORTED, "%s: hq %% hkv != 0 (%d, %d)", fn, s->hq, s->hkv);
+  if (s->d != 64 && s->d != 128) return fail(SEGATTN_E_UNSUPPORTED, "%s: d = %d not in {64, 128}", fn, s->d);
+  if (s->in_dtype != SEGATTN_BF16 && s->in_dtype != SEGATTN_F32)
+    return fail(SEGATTN_E_INVALID, "%s: in_dtype %d unknown", fn, s->in_dtype);
+  if (!(std::isfinite(s->scale) && s->scale > 0.f)) return fail(SEGATTN_E_INVALID, "%s: scale must be finite and > 0", fn);
+  // Element offsets are 64-bit in the kernels; rows times heads must stay
+  // within int64 comfortably (always true below 2^31 tokens and 2^16 heads).
+  if (s->hq > 65536 || s->hkv > 65536) return fail(SEGATTN_E_RANGE, "%s: too many heads", fn);
+  return SEGATTN_OK;
+}
+
+// Per-item ranges.  Sequence-local indices must fit int32 once offset.
+int check_items(const segattn_shape *s, const segattn_item *items, int32_t n, const char *fn) {
+  if (!items) return fail(SEGATTN_E_INVALID, "%s: items is NULL", fn);
+  if (n < 1) return fail(SEGATTN_E_INVALID, "%s: n_items = %d < 1", fn, n);
+  for (int32_t i = 0; i < n; ++i) {
+    const segattn_item &it = items[i];
+    if (it.seq_off < 0 || it.q_lo < 0 || it.k_lo < 0)
+      return fail(SEGATTN_E_RANGE, "%s: item %d has a negative index", fn, i);
+    if (it.q_hi <= it.q_lo) return fail(SEGATTN_E_RANGE, "%s: item %d has an empty query range", fn, i);
+    if (it.k_hi <= it.k_lo) return fail(SEGATTN_E_RANGE, "%s: item %d has an empty key range", fn, i);
+    if (it.k_hi > it.q_hi)
+      return fail(SEGATTN_E_RANGE, "%s: item %d: k_hi %lld > q_hi %lld (keys no query of the item can see)", fn, i,
+                  (long long)it.k_hi, (long long)it.q_hi);
+    if (it.seq_off > s->tokens || it.q_hi > s->tokens - it.seq_off)
+      return fail(SEGATTN_E_RANGE, "%s: item %d reaches beyond tokens = %lld", fn, i, (long long)s->tokens);
+  }
+  return SEGATTN_OK;
+}
+
+struct Range {
+  int64_t lo, hi;  // global, half-open
+  int32_t idx;
+};
+
+// Forward items must have pairwise disjoint global query ranges.
+int check_disjoint_q(const segattn_item *items, int32_t n, const char *fn) {
+  std::vector<Range> r(n);
+  for (int32_t i = 0; i < n; ++i) r[i] = {items[i].seq_off + items[i].q_lo, items[i].seq_off + items[i].q_hi, i};
+  std::sort(r.begin(), r.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+  for (int32_t i = 1; i < n; ++i)
+    if (r[i].lo < r[i - 1].hi)
+      return fail(SEGATTN_E_INVALID, "%s: items %d and %d have overlapping query rows", fn, r[i - 1].idx, r[i].idx);
+  return SEGATTN_OK;
+}
+
+int device_error(hipError_t e, const char *fn) {
+  return fail(SEGATTN_E_DEVICE, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------ forward table
+// Items sorted by the cost of their heaviest query tile (keys visible to its
+// last row), heaviest first; each item's tiles run from its last rows to its
+// first, so the whole unit order is heaviest-first for a single sequence.
+struct FwdPlan {
+  std::vector<int32_t> words;
+  int32_t n_units = 0;
+};
+
+void build_fwd_plan(const segattn_item *items, int32_t n, FwdPlan &p) {
+  std::vector<int32_t> order(n);
+  for (int32_t i = 0; i < n; ++i) order[i] = i;
+  auto cost = [&](int32_t i) { return std::min(items[i].k_hi, items[i].q_hi) - items[i].k_lo; };
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+  p.words.assign((size_t)n * kItemWords, 0);
+  int64_t unit = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    const segattn_item &it = items[order[r]];
+    int32_t *w = &p.words[(size_t)r * kItemWords];
+    w[0] = (int32_t)it.seq_off;
+    w[1] = (int32_t)it.q_lo;
+    w[2] = (int32_t)it.q_hi;
+    w[3] = (int32_t)it.k_lo;
+    w[4] = (int32_t)it.k_hi;
+    w[5] = (int32_t)unit;
+    unit += (it.q_hi - it.q_lo + kFwdBM - 1) / kFwdBM;
+  }
+  p.n_units = (int32_t)unit;
+}
+
+size_t fwd_ws_bytes(int32_t n) { return align_up((size_t)n * kItemWords * sizeof(int32_t)); }
+
+// ----------------------------------------------------------- backward table
+struct BwdPlan {
+  std::vector<int32_t> items, kvg, qg;
+  int32_t n_kv_units = 0, n_q_units = 0;
+};
+
+int build_bwd_plan(const segattn_item *items, int32_t n, BwdPlan &p, const char *fn) {
+  // q groups: runs of adjacent items with identical query ranges.
+  struct QG {
+    int32_t first, count;
+    int64_t lo, hi;  // global rows
+    int64_t cost;
+  };
+  std::vector<QG> qgs;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t lo = items[i].seq_off + items[i].q_lo, hi = items[i].seq_off + items[i].q_hi;
+    if (!qgs.empty() && qgs.back().lo == lo && qgs.back().hi == hi &&
+        items[qgs.back().first].seq_off == items[i].seq_off) {
+      qgs.back().count++;
+    } else {
+      qgs.push_back({i, 1, lo, hi, 0});
+    }
+  }
+  {
+    std::vector<Range> r(qgs.size());
+    for (size_t i = 0; i < qgs.size(); ++i) r[i] = {qgs[i].lo, qgs[i].hi, qgs[i].first};
+    std::sort(r.begin(), r.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < r.size(); ++i)
+      if (r[i].lo < r[i - 1].hi)
+        return fail(SEGATTN_E_INVALID,
+                    "%s: items %d and %d overlap in query rows without being adjacent items of one query range", fn,
+                    r[i - 1].idx, r[i].idx);
+  }
+  // kv groups: per sequence, the union of the items' key ranges as disjoint
+  // intervals (rows outside every key range are never written).
+  struct KG {
+    int64_t seq_off, kb, ke, qmax;
+  };
+  std::vector<KG> kgs;
+  {
+    std::vector<int32_t> idx(n);
+    for (int32_t i = 0; i < n; ++i) idx[i] = i;
+    std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+      if (items[a].seq_off != items[b].seq_off) return items[a].seq_off < items[b].seq_off;
+      return items[a].k_lo < items[b].k_lo;
+    });
+    for (int32_t t = 0; t < n; ++t) {
+      const segattn_item &it = items[idx[t]];
+      if (!kgs.empty() && kgs.back().seq_off == it.seq_off && it.k_lo <= kgs.back().ke) {
+        kgs.back().ke = std::max(kgs.back().ke, it.k_hi);
+        kgs.back().qmax = std::max(kgs.back().qmax, it.q_hi);
+      } else {
+        kgs.push_back({it.seq_off, it.k_lo, it.k_hi, it.q_hi});
+      }
+    }
+    // A key interval of one sequence also bounds the query rows that matter
+    // to it: the latest q_hi among the sequence's items.
+    for (auto &g : kgs) {
+      int64_t qm = 0;
+      for (int32_t i = 0; i < n; ++i)
+        if (items[i].seq_off == g.seq_off) qm = std::max(qm, items[i].q_hi);
+      g.qmax = qm;
+    }
+  }
+  // Heaviest work first: kv groups by the rows that can see their first key,
+  // q groups by the keys visible to their last row.
+  std::stable_sort(kgs.begin(), kgs.end(), [](const KG &a, const KG &b) { return a.qmax - a.kb > b.qmax - b.kb; });
+  for (auto &q : qgs) {
+    int64_t c = 0;
+    for (int32_t i = q.first; i < q.first + q.count; ++i) c += std::min(items[i].k_hi, items[i].q_hi) - items[i].k_lo;
+    q.cost = c;
+  }
+  std::stable_sort(qgs.begin(), qgs.end(), [](const QG &a, const QG &b) { return a.cost > b.cost; });
+
+  p.items.assign((size_t)n * kItemWords, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t *w = &p.items[(size_t)i * kItemWords];
+    w[0] = (int32_t)items[i].seq_off;
+    w[1] = (int32_t)items[i].q_lo;
+    w[2] = (int32_t)items[i].q_hi;
+    w[3] = (int32_t)items[i].k_lo;
+    w[4] = (int32_t)items[i].k_hi;
+  }
+  p.kvg.clear();
+  int64_t u = 0;
+  for (auto &g : kgs) {
+    p.kvg.insert(p.kvg.end(), {(int32_t)g.seq_off, (int32_t)g.kb, (int32_t)g.ke, (int32_t)u});
+    u += (g.ke - g.kb + kBwdKvBN - 1) / kBwdKvBN;
+  }
+  p.n_kv_units = (int32_t)u;
+  p.qg.clear();
+  u = 0;
+  for (auto &q : qgs) {
+    p.qg.insert(p.qg.end(), {q.first, q.count, (int32_t)u, 0});
+    u += (q.hi - q.lo + kBwdQBM - 1) / kBwdQBM;
+  }
+  p.n_q_units = (int32_t)u;
+  return SEGATTN_OK;
+}
+
+size_t bwd_delta_bytes(const segattn_shape *s) { return align_up((size_t)s->hq * (size_t)s->tokens * sizeof(float)); }
+
+size_t bwd_ws_bytes(const segattn_shape *s, const BwdPlan &p) {
+  return bwd_delta_bytes(s) + align_up(p.items.size() * 4) + align_up(p.kvg.size() * 4) + align_up(p.qg.size() * 4);
+}
+
+}  // namespace
+
+// ================================================================== forward
+
+extern "C" int segattn_fwd_workspace(const segattn_shape *shape, const segattn_item *items, int32_t n_items,
+                                     size_t *bytes) {
+  clear_error();
+  static const char *fn = "segattn_fwd_workspace";
+  if (!bytes) return fail(SEGATTN_E_INVALID, "%s: bytes is NULL", fn);
+  if (int rc = check_shape(shape, fn)) return rc;
+  if (int rc = check_items(shape, items, n_items, fn)) return rc;
+  *bytes = fwd_ws_bytes(n_items);
+  return SEGATTN_OK;
+}
+
+extern "C" int segattn_fwd(const segattn_shape *shape, const void *q, const void *k, const void *v,
+                           const segattn_item *items, int32_t n_items, void *o, int32_t o_dtype, float *lse,
+                           uint32_t flags, void *workspace, size_t ws_bytes, void *stream) {
+  clear_error();
+  static const char *fn = "segattn_fwd";
+  if (int rc = check_shape(shape, fn)) return rc;
+  if (int rc = check_ptr(q, fn, "q")) return rc;
+  if (int rc = check_ptr(k, fn, "k")) return rc;
+  if (int rc = check_ptr(v, fn, "v")) return rc;
+  if (int rc = check_ptr(o, fn, "o")) return rc;
+  if (int rc = check_ptr(lse, fn, "lse")) return rc;
+  if (o_dtype != SEGATTN_BF16 && o_dtype != SEGATTN_F32) return fail(SEGATTN_E_INVALID, "%s: o_dtype %d unknown", fn, o_dtype);
+  if (flags & ~SEGATTN_MERGE_INTO) return fail(SEGATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if ((flags & SEGATTN_MERGE_INTO) && o_dtype != SEGATTN_F32)
+    return fail(SEGATTN_E_INVALID, "%s: SEGATTN_MERGE_INTO needs an fp32 output", fn);
+  if (int rc = check_items(shape, items, n_items, fn)) return rc;
+  if (int rc = check_disjoint_q(items, n_items, fn)) return rc;
+  const size_t need = fwd_ws_bytes(n_items);
+  if (!workspace || ws_bytes < need)
+    return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
+
+  FwdPlan plan;
+  build_fwd_plan(items, n_items, plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t *table = static_cast<int32_t *>(workspace);
+  if (hipError_t e = launch_upload(table, plan.words.data(), (int64_t)plan.words.size(), s)) return device_error(e, fn);
+
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.items = table;
+  a.n_items = n_items;
+  a.n_units = plan.n_units;
+  a.tokens = shape->tokens;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.scale_log2 = shape->scale * 1.4426950408889634f;
+  a.merge = (flags & SEGATTN_MERGE_INTO) ? 1 : 0;
+  if ((int64_t)a.n_units * a.hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
+  if (hipError_t e = launch_fwd(a, shape->d, shape->in_dtype, o_dtype, s)) return device_error(e, fn);
+  return SEGATTN_OK;
+}
+
+// ==================================================================== merge
+
+extern "C" int segattn_merge(int64_t rows, int32_t h, int32_t d, int64_t lse_stride, const float *o_a,
+                             const float *lse_a, const float *o_b, const float *lse_b, float *o_out, float *lse_out,
+                             void *stream) {
+  clear_error();
+  static const char *fn = "segattn_merge";
+  if (rows < 1 || h < 1 || d < 4 || d % 4) return fail(SEGATTN_E_INVALID, "%s: rows, h >= 1 and d a multiple of 4", fn);
+  if (lse_stride < rows) return fail(SEGATTN_E_INVALID, "%s: lse_stride < rows", fn);
+  if (rows > (int64_t)1 << 40 || (int64_t)h * lse_stride > (int64_t)1 << 40)
+    return fail(SEGATTN_E_RANGE, "%s: sizes too large", fn);
+  for (auto pr : {std::make_pair((const void *)o_a, "o_a"), std::make_pair((const void *)o_b, "o_b"),
+                  std::make_pair((const void *)o_out, "o_out")})
+    if (int rc = check_ptr(pr.first, fn, pr.second)) return rc;
+  if (!lse_a || !lse_b || !lse_out) return fail(SEGATTN_E_INVALID, "%s: lse pointer is NULL", fn);
+  if (((uintptr_t)lse_a | (uintptr_t)lse_b | (uintptr_t)lse_out) & 3u)
+    return fail(SEGATTN_E_INVALID, "%s: lse pointers must be 4-byte aligned", fn);
+  MergeArgs a{rows, h, d, lse_stride, o_a, lse_a, o_b, lse_b, o_out, lse_out};
+  if (hipError_t e = launch_merge(a, static_cast<hipStream_t>(stream))) return device_error(e, fn);
+  return SEGATTN_OK;
+}
+
+// ================================================================= backward
+
+extern "C" int segattn_bwd_workspace(const segattn_shape *shape, const segattn_item *items, int32_t n_items,
+                                     size_t *bytes) {
+  clear_error();
+  static const char *fn = "segattn_bwd_workspace";
+  if (!bytes) return fail(SEGATTN_E_INVALID, "%s: bytes is NULL", fn);
+  if (int rc = check_shape(shape, fn)) return rc;
+  if (int rc = check_items(shape, items, n_items, fn)) return rc;
+  BwdPlan plan;
+  if (int rc = build_bwd_plan(items, n_items, plan, fn)) return rc;
+  *bytes = bwd_ws_bytes(shape, plan);
+  return SEGATTN_OK;
+}
+
+extern "C" int segattn_bwd_preprocess(const segattn_shape *shape, const void *o, int32_t o_dtype, const void *d_o,
+                                      const segattn_item *items, int32_t n_items, void *workspace, size_t ws_bytes,
+                                      void *stream) {
+  clear_error();
+  static const char *fn = "segattn_bwd_preprocess";
+  if (int rc = check_shape(shape, fn)) return rc;
+  if (int rc = check_ptr(o, fn, "o")) return rc;
+  if (int rc = check_ptr(d_o, fn, "d_o")) return rc;
+  if (o_dtype != SEGATTN_BF16 && o_dtype != SEGATTN_F32) return fail(SEGATTN_E_INVALID, "%s: o_dtype %d unknown", fn, o_dtype);
+  if (int rc = check_items(shape, items, n_items, fn)) return rc;
+  BwdPlan plan;
+  if (int rc = build_bwd_plan(items, n_items, plan, fn)) return rc;
+  const size_t need = bwd_ws_bytes(shape, plan);
+  if (!workspace || ws_bytes < need)
+    return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
+  PreArgs a{o, d_o, static_cast<float *>(workspace), shape->tokens, shape->hq};
+  if (hipError_t e = launch_bwd_pre(a, shape->d, o_dtype, shape->in_dtype, static_cast<hipStream_t>(stream)))
+    return device_error(e, fn);
+  return SEGATTN_OK;
+}
+
+extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const void *v, const void *o,
+                           int32_t o_dtype, const float *lse, const void *d_o, const segattn_item *items,
+                           int32_t n_items, void *dq, void *dk, void *dv, int32_t g_dtype, uint32_t flags,
+                           void *workspace, size_t ws_bytes, void *stream) {
+  clear_error();
+  static const char *fn = "segattn_bwd";
+  if (int rc = check_shape(shape, fn)) return rc;
+  const void *ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
+  const char *names[] = {"q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i)
+    if (int rc = check_ptr(ptrs[i], fn, names[i])) return rc;
+  if (o_dtype != SEGATTN_BF16 && o_dtype != SEGATTN_F32) return fail(SEGATTN_E_INVALID, "%s: o_dtype %d unknown", fn, o_dtype);
+  if (g_dtype != SEGATTN_BF16 && g_dtype != SEGATTN_F32) return fail(SEGATTN_E_INVALID, "%s: g_dtype %d unknown", fn, g_dtype);
+  if (flags & ~(SEGATTN_ACCUMULATE | SEGATTN_D_READY)) return fail(SEGATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if ((flags & SEGATTN_ACCUMULATE) && g_dtype != SEGATTN_F32)
+    return fail(SEGATTN_E_INVALID, "%s: SEGATTN_ACCUMULATE needs fp32 gradients", fn);
+  if (int rc = check_items(shape, items, n_items, fn)) return rc;
+  BwdPlan plan;
+  if (int rc = build_bwd_plan(items, n_items, plan, fn)) return rc;
+  const size_t need = bwd_ws_bytes(shape, plan);
+  if (!workspace || ws_bytes < need)
+    return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
+  if ((int64_t)plan.n_kv_units * shape->hkv > 0x7fffffffLL || (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL)
+    return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  float *delta = reinterpret_cast<float *>(ws);
+  size_t off = bwd_delta_bytes(shape);
+  int32_t *d_items = reinterpret_cast<int32_t *>(ws + off);
+  off += align_up(plan.items.size() * 4);
+  int32_t *d_kvg = reinterpret_cast<int32_t *>(ws + off);
+  off += align_up(plan.kvg.size() * 4);
+  int32_t *d_qg = reinterpret_cast<int32_t *>(ws + off);
+
+  if (!(flags & SEGATTN_D_READY)) {
+    PreArgs pa{o, d_o, delta, shape->tokens, shape->hq};
+    if (hipError_t e = launch_bwd_pre(pa, shape->d, o_dtype, shape->in_dtype, s)) return device_error(e, fn);
+  }
+  if (hipError_t e = launch_upload(d_items, plan.items.data(), (int64_t)plan.items.size(), s)) return device_error(e, fn);
+  if (hipError_t e = launch_upload(d_kvg, plan.kvg.data(), (int64_t)plan.kvg.size(), s)) return device_error(e, fn);
+  if (hipError_t e = launch_upload(d_qg, plan.qg.data(), (int64_t)plan.qg.size(), s)) return device_error(e, fn);
+
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.items = d_items;
+  a.kvg = d_kvg;
+  a.qg = d_qg;
+  a.n_items = n_items;
+  a.n_kvg = (int32_t)(plan.kvg.size() / 4);
+  a.n_qg = (int32_t)(plan.qg.size() / 4);
+  a.n_kv_units = plan.n_kv_units;
+  a.n_q_units = plan.n_q_units;
+  a.tokens = shape->tokens;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.scale = shape->scale;
+  a.scale_log2 = shape->scale * 1.4426950408889634f;
+  a.accumulate = (flags & SEGATTN_ACCUMULATE) ? 1 : 0;
+  if (hipError_t e = launch_bwd_dkdv(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
+  if (hipError_t e = launch_bwd_dq(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
+  return SEGATTN_OK;
+}

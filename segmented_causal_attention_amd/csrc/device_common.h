@@ -1,0 +1,89 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 packing,
+// global/LDS 16-byte accesses and wavefront reductions.
+//
+// MFMA operand layout used throughout (v_mfma_f32_16x16x32_bf16, wave64):
+//   A (16 x 32, rows m, depth k): lane l supplies A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B (32 x 16, depth k, cols n): lane l supplies B[8 * (l / 16) + j][l % 16]
+//   C (16 x 16):                  lane l holds   C[4 * (l / 16) + i][l % 16], i = 0..3
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace segattn {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even) packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4 &a, const f32x4 &b) {
+  u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+             pack_bf16x2(b[2], b[3])};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 consecutive input elements as packed bf16 (4 dwords).  For fp32 input
+// the values are rounded to nearest-even bf16 here, while staging.
+template <typename InT>
+__device__ __forceinline__ u32x4 load8(const InT *p);
+
+template <>
+__device__ __forceinline__ u32x4 load8<__bf16>(const __bf16 *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <>
+__device__ __forceinline__ u32x4 load8<float>(const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  return (u32x4){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                 pack_bf16x2(b[2], b[3])};
+}
+
+// Byte-select of two dwords: result byte i = byte sel_i of {hi:lo}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// low bf16 of x and low bf16 of y -> (y.lo << 16) | x.lo
+__device__ __forceinline__ uint32_t join_lo(uint32_t x, uint32_t y) { return perm(y, x, 0x05040100u); }
+// high bf16 of x and high bf16 of y -> (y.hi << 16) | x.hi
+__device__ __forceinline__ uint32_t join_hi(uint32_t x, uint32_t y) { return perm(y, x, 0x07060302u); }
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+}  // namespace dev
+}  // namespace segattn

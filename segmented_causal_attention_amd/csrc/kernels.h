@@ -1,0 +1,93 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the HIP
+// kernels.  Not installed; no torch or HIP types appear in segattn.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace segattn {
+
+// Device item table: one row of kItemWords int32 per work item.
+//   [0] seq_off  [1] q_lo  [2] q_hi  [3] k_lo  [4] k_hi   (sequence-local)
+//   [5] unit_begin: first work unit of this item in the launch's unit order
+//   [6] aux0  [7] aux1  (per-kernel meaning, see below)
+constexpr int kItemWords = 8;
+
+// Forward tile shape: 256 query rows per workgroup (4 waves x 64 rows),
+// 64 keys per K/V tile staged through LDS.
+constexpr int kFwdBM = 256;
+constexpr int kFwdBN = 64;
+
+// Backward tile shapes.
+//   dK/dV kernel: 128 keys per workgroup (4 waves x 32 keys), 64 query rows
+//                 per staged Q/dO tile.
+//   dQ kernel:    128 query rows per workgroup (4 waves x 32 rows), 64 keys
+//                 per staged K/V tile.
+constexpr int kBwdKvBN = 128;
+constexpr int kBwdKvBM = 64;
+constexpr int kBwdQBM = 128;
+constexpr int kBwdQBN = 64;
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *items;  // device table, n_items rows
+  int32_t n_items;
+  int32_t n_units;       // query tiles over all items
+  int64_t tokens;
+  int32_t hq, hkv;
+  float scale_log2;      // scale * log2(e)
+  int32_t merge;         // 1: merge into the fp32 (O, LSE) already in o/lse
+};
+
+// D[h][t] = <dO[t,h,:], O[t,h,:]> for every token row.
+struct PreArgs {
+  const void *o, *d_o;
+  float *delta;
+  int64_t tokens;
+  int32_t hq;
+};
+
+// Backward tables.  Items keep the caller's order (the kernels walk them in
+// reverse).  kv units: one per (kv group, 128-key tile); kv group g covers
+// keys [kb, ke) of one sequence, stored as rows of kvg (4 int32):
+//   [0] seq_off [1] kb [2] ke [3] unit_begin
+// q units: one per (q group, 128-row tile); q group = a run of adjacent items
+// with identical query ranges, stored as rows of qg (4 int32):
+//   [0] first item  [1] item count  [2] unit_begin  [3] unused
+struct BwdArgs {
+  const void *q, *k, *v, *d_o;
+  const float *lse, *delta;
+  void *dq, *dk, *dv;
+  const int32_t *items, *kvg, *qg;
+  int32_t n_items, n_kvg, n_qg;
+  int32_t n_kv_units, n_q_units;
+  int64_t tokens;
+  int32_t hq, hkv;
+  float scale, scale_log2;
+  int32_t accumulate;    // 1: fp32 outputs, add to them
+};
+
+struct MergeArgs {
+  int64_t rows;
+  int32_t h, d;
+  int64_t lse_stride;
+  const float *o_a, *lse_a, *o_b, *lse_b;
+  float *o_out, *lse_out;
+};
+
+// Launchers (return the hipError_t of the launch).  Template arguments are
+// resolved inside the .hip files from the runtime dtype codes.
+hipError_t launch_fwd(const FwdArgs &a, int d, int in_dtype, int o_dtype, hipStream_t s);
+hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+// Copies n int32 words from host memory into dst (device) through kernel
+// arguments: stream-ordered, graph-capturable, no pageable-memory copy.
+hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStream_t s);
+
+}  // namespace segattn

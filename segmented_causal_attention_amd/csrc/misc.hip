@@ -1,0 +1,147 @@
+// Memory-bound kernels: log-sum-exp merge of partial results, the backward
+// row reduction D = <dO, O>, and the stream-ordered table upload.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace segattn {
+namespace dev {
+
+// ---------------------------------------------------------------- merge
+// Softmax over a disjoint union of key sets A and B (InfiniPipe section II-A:
+// the ring's partial results are combined by online self-attention):
+//   m = max(l_a, l_b);  m = -inf -> (0, -inf);  w = e^(l - m);
+//   LSE = m + log(w_a + w_b),  O = (w_a O_a + w_b O_b) / (w_a + w_b).
+// One thread per 4 consecutive floats of a (row, head) vector; the d/4
+// threads of one vector sit in one wavefront, so an in-place merge reads the
+// old LSE in every lane before any lane stores the new one.
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int cpv = a.d >> 2;  // float4 chunks per (row, head) vector
+  const int64_t total = a.rows * a.h * cpv;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int64_t vec = idx / cpv;
+    const int c = (int)(idx - vec * cpv);
+    const int64_t r = vec / a.h;
+    const int hh = (int)(vec - r * a.h);
+    const int64_t li = (int64_t)hh * a.lse_stride + r;
+    const float la = a.lse_a[li], lb = a.lse_b[li];
+    const float m = fmaxf(la, lb);
+    const f32x4 oa = *reinterpret_cast<const f32x4 *>(a.o_a + vec * a.d + 4 * c);
+    const f32x4 ob = *reinterpret_cast<const f32x4 *>(a.o_b + vec * a.d + 4 * c);
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    float lse = kNegInf;
+    if (m != kNegInf) {
+      const float wa = fast_exp2((la - m) * kLog2e), wb = fast_exp2((lb - m) * kLog2e);
+      const float den = wa + wb, inv = 1.f / den;
+      out = oa * (wa * inv) + ob * (wb * inv);
+      lse = m + fast_log2(den) * kLn2;
+    }
+    *reinterpret_cast<f32x4 *>(a.o_out + vec * a.d + 4 * c) = out;
+    if (c == 0) a.lse_out[li] = lse;
+  }
+}
+
+// ------------------------------------------------------------- D = <dO, O>
+// One 8-element chunk per thread, d/8 threads per (token, head) row reduced
+// with xor shuffles inside the wavefront.
+template <int D, typename OT, typename GT>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
+  constexpr int CPR = D / 8;  // chunks per row: 16 or 8
+  const int64_t rows = a.tokens * a.hq;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const OT *og = static_cast<const OT *>(a.o);
+  const GT *dg = static_cast<const GT *>(a.d_o);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < rows * CPR; idx += stride) {
+    const int64_t row = idx / CPR;  // row = t * hq + h
+    const int c = (int)(idx - row * CPR);
+    float acc = 0.f;
+    const OT *op = og + row * D + 8 * c;
+    const GT *gp = dg + row * D + 8 * c;
+    float ov[8], gv[8];
+    if constexpr (sizeof(OT) == 4) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(op), x1 = *reinterpret_cast<const f32x4 *>(op + 4);
+      for (int i = 0; i < 4; ++i) { ov[i] = x0[i]; ov[4 + i] = x1[i]; }
+    } else {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(op);
+      for (int i = 0; i < 4; ++i) { ov[2 * i] = bf16_lo(w[i]); ov[2 * i + 1] = bf16_hi(w[i]); }
+    }
+    if constexpr (sizeof(GT) == 4) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(gp), x1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+      for (int i = 0; i < 4; ++i) { gv[i] = x0[i]; gv[4 + i] = x1[i]; }
+    } else {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(gp);
+      for (int i = 0; i < 4; ++i) { gv[2 * i] = bf16_lo(w[i]); gv[2 * i + 1] = bf16_hi(w[i]); }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(ov[i], gv[i], acc);
+#pragma unroll
+    for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0) {
+      const int64_t t = row / a.hq;
+      const int h = (int)(row - t * a.hq);
+      a.delta[(int64_t)h * a.tokens + t] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- upload
+constexpr int kUploadWords = 248;
+struct UploadChunk {
+  int32_t n;
+  int32_t pad;
+  int32_t w[kUploadWords];
+};
+
+__global__ __launch_bounds__(256) void upload_kernel(int32_t *dst, UploadChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.n) dst[i] = c.w[i];
+}
+
+static unsigned grid_for(int64_t work, int64_t per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g > 256 * 64) g = 256 * 64;  // grid-stride beyond 64 workgroups per CU
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace dev
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
+  using namespace dev;
+  const int64_t work = a.rows * a.h * (a.d / 4);
+  hipLaunchKernelGGL(merge_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s) {
+  using namespace dev;
+  const int64_t work = a.tokens * a.hq * (d / 8);
+  const dim3 grid(grid_for(work, 256)), block(256);
+  const bool ob = o_dtype == 0, gb = in_dtype == 0;
+#define SEGATTN_PRE(DD, OT, GT) hipLaunchKernelGGL((bwd_pre_kernel<DD, OT, GT>), grid, block, 0, s, a)
+  if (d == 128) {
+    if (ob) { if (gb) SEGATTN_PRE(128, __bf16, __bf16); else SEGATTN_PRE(128, __bf16, float); }
+    else { if (gb) SEGATTN_PRE(128, float, __bf16); else SEGATTN_PRE(128, float, float); }
+  } else {
+    if (ob) { if (gb) SEGATTN_PRE(64, __bf16, __bf16); else SEGATTN_PRE(64, __bf16, float); }
+    else { if (gb) SEGATTN_PRE(64, float, __bf16); else SEGATTN_PRE(64, float, float); }
+  }
+#undef SEGATTN_PRE
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStream_t s) {
+  using namespace dev;
+  for (int64_t off = 0; off < n; off += kUploadWords) {
+    UploadChunk c;
+    c.n = (int32_t)((n - off) < kUploadWords ? (n - off) : kUploadWords);
+    c.pad = 0;
+    for (int i = 0; i < c.n; ++i) c.w[i] = words[off + i];
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, dst + off, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace segattn
