@@ -22,6 +22,7 @@ invariants); none is "parity unpinned".
 
 from .planner import (  # noqa: F401
     tri,
+    boundary,
     segment_work,
     partition,
     partition_varlen,

@@ -48,6 +48,16 @@ def _least_b_reaching(target_times_n: int, n: int, S: int) -> int:
     return lo
 
 
+def boundary(i: int, N: int, S: int) -> int:
+    """Inner boundary i of the N-way partition of S tokens: the integer b in
+    [0, S] minimising |N*T(b) - i*T(S)| (ties to the smaller b)."""
+    goal = i * tri(S)  # compare N*T(b) against i*T(S) without division
+    b = _least_b_reaching(goal, N, S)
+    if b > 0 and abs(N * tri(b - 1) - goal) <= abs(N * tri(b) - goal):
+        return b - 1
+    return b
+
+
 def partition(S: int, N: int) -> list[int]:
     """FLOPs-balanced partition of one causal sequence of length S into N
     segments; returns the boundaries b_0 = 0 < b_1 < ... < b_N = S.
@@ -70,19 +80,7 @@ def partition(S: int, N: int) -> list[int]:
         raise ValueError("N must be >= 1")
     if S < N:
         raise ValueError("S must be >= N")
-    total = tri(S)
-    bounds = [0]
-    for i in range(1, N):
-        goal = i * total  # compare N*T(b) against i*T(S) without division
-        b = _least_b_reaching(goal, N, S)
-        best = b
-        if b > 0:
-            below = abs(N * tri(b - 1) - goal)
-            at = abs(N * tri(b) - goal)
-            if below <= at:  # tie -> the smaller boundary
-                best = b - 1
-        bounds.append(best)
-    bounds.append(S)
+    bounds = [0] + [boundary(i, N, S) for i in range(1, N)] + [S]
     for i in range(N):
         if bounds[i + 1] <= bounds[i]:
             raise ValueError(f"empty segment {i} for S={S}, N={N}")
@@ -100,7 +98,7 @@ def partition_varlen(cu_seqlens, max_slice: int):
     item attending to itself.  A longer one is cut with ``partition(L, n)``
     for the least n >= 2 whose first (longest) slice is <= max_slice; each
     slice [lo, hi) becomes an item with keys [0, hi).  Empty sequences give
-    no item.
+    no item.  Only the chosen cut has to be free of empty slices.
     """
     max_slice = int(max_slice)
     if max_slice < 1:
@@ -119,13 +117,11 @@ def partition_varlen(cu_seqlens, max_slice: int):
             items.append((off, 0, L, 0, L))
             continue
         n = 2
-        while True:
+        while boundary(1, n, L) > max_slice:  # first (longest) slice too long
+            n += 1
             if n > L:
                 raise ValueError(f"cannot slice a sequence of length {L}")
-            b = partition(L, n)  # raises on an empty slice
-            if b[1] - b[0] <= max_slice:
-                break
-            n += 1
+        b = partition(L, n)  # raises if a slice of this cut is empty
         for i in range(n):
             items.append((off, b[i], b[i + 1], 0, b[i + 1]))
     return items
