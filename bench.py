@@ -1,0 +1,250 @@
+"""Benchmark of the segmented causal attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu-baseline]
+
+One step = one pass of the whole path over one synthetic batch, inputs resident
+in HBM: the host planner cuts the sequence into FLOPs-balanced segments, the
+forward runs every segment's queries against the resident K/V prefix
+(segattn_fwd; ring workloads add the log-sum-exp merges), the backward
+reduction D = <dO, O> runs (segattn_bwd_preprocess), and the backward walks the
+items in reverse order (segattn_bwd).  The default workload is one causal
+attention layer of 32 heads x 128 dims over 32768 tokens in 8 segments, bf16.
+
+Throughput is algorithmic: 14 * d * pairs * Hq FLOP per step (forward
+4 d pairs, backward 10 d pairs per head; pairs = visible causal (query, key)
+pairs; masked and recomputed work is not counted), divided by the GPU time of
+the timed steps (HIP events on the stream the library launches on).
+
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with an
+error message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # CUs x clock x dense bf16 FLOP/clk/CU = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=32768,
+                   help="token prefix of one head timed for the CPU oracle baseline")
+    return p.parse_args()
+
+
+def visible_pairs(lengths):
+    return sum(L * (L + 1) // 2 for L in lengths)
+
+
+class Workload:
+    """Inputs, items and preallocated outputs of one benchmark workload."""
+
+    def __init__(self, name, torch, sa, synth):
+        w = synth.WORKLOADS[name]
+        self.name, self.w = name, w
+        self.hq, self.hkv, self.d = w["hq"], w["hkv"], w["d"]
+        if name == "c4":
+            lens = synth.lognormal_lengths(w["seed"], total=w["T"])
+            self.cu = synth.cu_seqlens(lens)
+            self.T = int(self.cu[-1])
+            self.lengths = lens
+        else:
+            self.T = w["S"]
+            self.lengths = [w["S"]]
+            self.cu = None
+        t = synth.gen_tensors(w["seed"], self.T, self.hq, self.hkv, self.d, dtype="bf16", device="cuda")
+        self.q, self.k, self.v, self.do = t["q"], t["k"], t["v"], t["do"]
+        self.ring = name == "c3"
+        o_dtype = torch.float32 if self.ring else torch.bfloat16
+        self.o = torch.empty((self.T, self.hq, self.d), dtype=o_dtype, device="cuda")
+        self.lse = torch.empty((self.hq, self.T), dtype=torch.float32, device="cuda")
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        self.items = self.plan()
+        shape = sa.make_shape(self.q, self.k)
+        self.fws = torch.empty(max(sa.segattn_fwd_workspace(shape, self.items), 16), dtype=torch.uint8,
+                               device="cuda")
+        self.bws = torch.empty(sa.segattn_bwd_workspace(shape, self.items[::-1].copy()), dtype=torch.uint8,
+                               device="cuda")
+        self.pairs = visible_pairs(self.lengths)
+        self.flops_fwd = 4 * self.d * self.pairs * self.hq
+        self.flops_bwd = 10 * self.d * self.pairs * self.hq
+        self.sa = sa
+
+    def plan(self):
+        sa, w = self.sa_mod(), self.w
+        if self.name == "c4":
+            return sa.segattn_partition_varlen(self.cu, w["max_slice"])
+        b = sa.segattn_partition(w["S"], w["N"])
+        if self.ring:
+            return sa.segattn_ring_items(b, w["block"])
+        return np.array([[0, b[i], b[i + 1], 0, b[i + 1]] for i in range(w["N"])], np.int64)
+
+    @staticmethod
+    def sa_mod():
+        import segmented_causal_attention_amd as sa
+        return sa
+
+
+def ring_steps(items):
+    by, order = {}, []
+    for it in items.tolist():
+        key = tuple(it[:3])
+        if key not in by:
+            by[key] = []
+            order.append(key)
+        by[key].append(it)
+    steps, s = [], 0
+    while True:
+        st = [by[k][s] for k in order if len(by[k]) > s]
+        if not st:
+            return steps
+        steps.append(np.array(st, np.int64))
+        s += 1
+
+
+def run_step(W, torch, ev=None):
+    """One pass of the path.  ev: optional list of 4 events recorded around
+    the forward, the D reduction and the backward."""
+    sa = W.sa
+    items = W.plan()  # host planner, part of the step
+    if ev:
+        ev[0].record()
+    if W.ring:
+        for s, step in enumerate(ring_steps(items)):
+            sa.segattn_fwd(W.q, W.k, W.v, step, o=W.o, lse=W.lse, merge_into=s > 0, workspace=W.fws)
+    else:
+        sa.segattn_fwd(W.q, W.k, W.v, items, o=W.o, lse=W.lse, workspace=W.fws)
+    if ev:
+        ev[1].record()
+    rev = items[::-1].copy()
+    sa.segattn_bwd_preprocess(W.q, W.k, W.o, W.do, rev, W.bws)
+    if ev:
+        ev[2].record()
+    sa.segattn_bwd(W.q, W.k, W.v, W.o, W.lse, W.do, rev, dq=W.dq, dk=W.dk, dv=W.dv, d_ready=True,
+                   workspace=W.bws)
+    if ev:
+        ev[3].record()
+
+
+def cpu_baseline(W, synth, tokens, heads=2):
+    """The float64 oracle on a bounded sample of the same workload: the
+    first `heads` heads over the first `tokens` tokens (one causal
+    sequence), forward + backward."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    tok = min(tokens, W.T)
+    hh = min(heads, W.hq)
+    hk = max(1, hh * W.hkv // W.hq)
+    q = synth.to_numpy_f32(W.q[:tok, :hh])
+    k = synth.to_numpy_f32(W.k[:tok, :hk])
+    v = synth.to_numpy_f32(W.v[:tok, :hk])
+    do = synth.to_numpy_f32(W.do[:tok, :hh])
+    scale = 1.0 / math.sqrt(W.d)
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, None, scale)
+    oracle.attention_bwd(q, k, v, do, None, scale)
+    dt = time.perf_counter() - t0
+    flops = 14 * W.d * (tok * (tok + 1) // 2) * hh
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, forward+backward of {hh} head(s) over the first {tok} tokens "
+                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s; cpu: {model}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import segmented_causal_attention_amd as sa
+    import synthetic_inputs as synth
+
+    torch.cuda.set_device(0)
+    W = Workload(args.workload, torch, sa, synth)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        run_step(W, torch)
+    torch.cuda.synchronize()
+
+    E = torch.cuda.Event
+    per = [[E(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(W, torch, per[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    fwd_ms = float(np.mean([p[0].elapsed_time(p[1]) for p in per]))
+    pre_ms = float(np.mean([p[1].elapsed_time(p[2]) for p in per]))
+    bwd_ms = float(np.mean([p[2].elapsed_time(p[3]) for p in per]))
+
+    flops = W.flops_fwd + W.flops_bwd
+    value = flops / (ms / 1e3) / 1e12
+    # Dominant launch: the backward main call (key-stationary dK/dV and
+    # query-stationary dQ kernels) or the forward call, whichever is longer.
+    if bwd_ms >= fwd_ms:
+        dom, dom_ms, dom_flops = "segattn_bwd (dkdv_kernel + dq_kernel)", bwd_ms, W.flops_bwd
+    else:
+        dom, dom_ms, dom_flops = "segattn_fwd (fwd_kernel)", fwd_ms, W.flops_fwd
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    out = {
+        "metric": "segmented causal attn fwd+bwd TFLOP/s and % of bf16 MFMA peak, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.w["name"], "tokens": W.T, "q_heads": W.hq, "kv_heads": W.hkv,
+                   "head_dim": W.d, "items": int(len(W.items)), "visible_pairs_per_head": int(W.pairs)},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "breakdown_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, synth, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
