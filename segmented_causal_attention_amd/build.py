@@ -28,7 +28,7 @@ HIP_SOURCES = ["fwd.hip", "bwd.hip", "misc.hip", "api.cpp"]
 # plain C++ (no HIP headers): the integer planner
 CPP_SOURCES = ["planner.cpp"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function", "-Werror=uninitialized"]
 
 
 def _run(cmd):

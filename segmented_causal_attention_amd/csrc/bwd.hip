@@ -14,25 +14,27 @@
 // dkdv_kernel: key-stationary.  A workgroup owns 128 keys of one KV head
 //   (4 waves x 32 keys; K and V in registers) and walks every (item, query
 //   head of the group, 64-row query tile) that can see them; per tile it
-//   recomputes S, P, dP, dS and accumulates dV and dK (4 products).
+//   recomputes S, P, dP, dS and accumulates dV and dK (4 products).  Q and
+//   dO tiles are staged row-major; the operands contracted over query rows
+//   are read with transposing LDS reads.
 // dq_kernel: query-stationary, like the forward.  A workgroup owns 128 query
 //   rows of one head (4 waves x 32 rows; Q and dO in registers) and walks the
 //   64-key tiles of every item of its query group; per tile it recomputes
 //   S^T, P, dP^T, dS^T and accumulates dQ^T (3 products).
 #include "device_common.h"
 #include "kernels.h"
+#include "tile.h"
 
 namespace segattn {
 namespace dev {
 
 template <int D>
 struct BwdCfg {
-  static constexpr int KS = D / 32;    // depth steps over the head dim
-  static constexpr int NT = D / 16;    // 16-wide head-dim tiles
-  static constexpr int ROW = D + 8;    // LDS row stride, row-major tiles (bf16)
-  static constexpr int TROW = 64 + 8;  // LDS row stride, transposed 64-row tiles (bf16)
-  static constexpr int STAGERS = 16 * (D / 8);  // threads staging a 64-row tile (4 rows x 8 dims each)
+  static constexpr int KS = D / 32;   // depth steps over the head dim
+  static constexpr int NT = D / 16;   // 16-wide head-dim tiles
+  static constexpr int TSZ = kTileRows * D;  // one swizzled 64-row tile (bf16 elements)
 };
+static_assert(kBwdKvBM == kTileRows && kBwdQBN == kTileRows, "backward tiles are 64-row LDS tiles");
 
 template <typename GT>
 __device__ __forceinline__ void put1(GT *p, float v, int accumulate);
@@ -81,47 +83,6 @@ __device__ __forceinline__ void map_head(int x, int nh, int &rank, int &h) {
   }
 }
 
-// Stages a 64-row tile of a [tokens][heads][D] tensor into LDS both
-// row-major (rows x D) and transposed (D x 64 rows).  Each staging thread
-// holds 4 consecutive rows x 8 dims.
-template <int D, typename InT>
-struct TileStager {
-  using C = BwdCfg<D>;
-  u32x4 r[4];
-  __device__ __forceinline__ void load(const InT *base, int64_t row0, int nvalid, int heads, int h, int tid) {
-    if (tid < C::STAGERS) {
-      const int rq = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * rq + i;
-        r[i] = rr < nvalid ? load8<InT>(base + ((row0 + rr) * heads + h) * D + 8 * dc) : (u32x4){0, 0, 0, 0};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *rowmajor, __bf16 *trans, int tid) const {
-    if (tid < C::STAGERS) {
-      const int rq = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(rowmajor + (4 * rq + i) * C::ROW + 8 * dc) = r[i];
-      if (trans) {
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int w = dd >> 1;
-          u32x2 pk;
-          if (dd & 1) {
-            pk[0] = join_hi(r[0][w], r[1][w]);
-            pk[1] = join_hi(r[2][w], r[3][w]);
-          } else {
-            pk[0] = join_lo(r[0][w], r[1][w]);
-            pk[1] = join_lo(r[2][w], r[3][w]);
-          }
-          *reinterpret_cast<u32x2 *>(trans + (8 * dc + dd) * C::TROW + 4 * rq) = pk;
-        }
-      }
-    }
-  }
-};
-
 // =================================================================== dK/dV
 
 struct KvStep {
@@ -134,8 +95,7 @@ template <int D, typename InT, typename GT>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int BQ = kBwdKvBM;  // 64 query rows per tile
-  constexpr int ROWS = BQ * C::ROW, TRANS = D * C::TROW;
-  constexpr int BUF = 2 * ROWS + 2 * TRANS;  // Q, dO row-major + transposed (bf16 elements)
+  constexpr int BUF = 2 * C::TSZ;  // Q tile, dO tile
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];  // [buf][lse2 | D][row]
 
@@ -150,6 +110,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const int kt1 = min(ke, kt0 + kBwdKvBN);
   const int G = a.hq / a.hkv;
   const int64_t T = a.tokens;
+  const int32_t *__restrict__ items = a.items;
+  const float *__restrict__ lse = a.lse;
+  const float *__restrict__ delta = a.delta;
+  const int hq = a.hq, hkv = a.hkv;
   const InT *qg = static_cast<const InT *>(a.q);
   const InT *kg = static_cast<const InT *>(a.k);
   const InT *vg = static_cast<const InT *>(a.v);
@@ -166,7 +130,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   for (int nk = 0; nk < 2; ++nk) {
     const int key = kw0 + 16 * nk + l16;
     const bool ok = key < kt1;
-    const int64_t base = ((int64_t)(seq_off + (ok ? key : kt0)) * a.hkv + g) * D + 8 * lg;
+    const int64_t base = ((int64_t)(seq_off + (ok ? key : kt0)) * hkv + g) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       kf[nk][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(kg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
@@ -184,17 +148,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
 
   // ---- step iterator over (item in reverse order, head, query tile)
-  auto item_sees = [&](int i) {
-    const int32_t *it = a.items + i * kItemWords;
+  auto item_sees = [&](int i) __attribute__((always_inline)) {
+    const int32_t *it = items + i * kItemWords;
     return it[0] == seq_off && it[3] < kt1 && it[4] > kt0 && it[2] > kt0;
   };
-  auto first_from = [&](int i) -> KvStep {
+  auto first_from = [&](int i) __attribute__((always_inline)) -> KvStep {
     for (; i >= 0; --i)
-      if (item_sees(i)) return KvStep{i, 0, max(a.items[i * kItemWords + 1], kt0)};
+      if (item_sees(i)) return KvStep{i, 0, max(items[i * kItemWords + 1], kt0)};
     return KvStep{-1, 0, 0};
   };
-  auto advance = [&](KvStep s) -> KvStep {
-    const int32_t *it = a.items + s.item * kItemWords;
+  auto advance = [&](KvStep s) __attribute__((always_inline)) -> KvStep {
+    const int32_t *it = items + s.item * kItemWords;
     s.qt0 += BQ;
     if (s.qt0 < it[2]) return s;
     if (++s.hh < G) {
@@ -204,31 +168,33 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     return first_from(s.item - 1);
   };
 
-  TileStager<D, InT> sq, sdo;
+  TileLoader<D, InT> lq, ldo;
   float st_lse = 0.f, st_d = 0.f;
-  auto gload = [&](const KvStep &s) {
-    const int32_t *it = a.items + s.item * kItemWords;
+  const int64_t qstride = (int64_t)hq * D;
+  auto stage = [&](const KvStep &s, int buf) __attribute__((always_inline)) {
+    const int32_t *it = items + s.item * kItemWords;
     const int h = g * G + s.hh;
     const int nvalid = min(BQ, it[2] - s.qt0);
     const int64_t row0 = (int64_t)seq_off + s.qt0;
-    sq.load(qg, row0, nvalid, a.hq, h, tid);
-    sdo.load(dg, row0, nvalid, a.hq, h, tid);
+    __bf16 *b = lds + buf * BUF;
+    lq.issue(b, qg + (row0 * hq + h) * D, qstride, nvalid, wave, lane);
+    ldo.issue(b + C::TSZ, dg + (row0 * hq + h) * D, qstride, nvalid, wave, lane);
     if (tid < BQ) {
       if (tid < nvalid) {
-        const float l = a.lse[(int64_t)h * T + row0 + tid];
+        const float l = lse[(int64_t)h * T + row0 + tid];
         // A row without visible keys (LSE = -inf) contributes nothing.
         st_lse = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        st_d = a.delta[(int64_t)h * T + row0 + tid];
+        st_d = delta[(int64_t)h * T + row0 + tid];
       } else {
         st_lse = __builtin_inff();
         st_d = 0.f;
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto commit = [&](int buf) __attribute__((always_inline)) {
     __bf16 *b = lds + buf * BUF;
-    sq.store(b, b + 2 * ROWS, tid);
-    sdo.store(b + ROWS, b + 2 * ROWS + TRANS, tid);
+    lq.commit(b, tid);
+    ldo.commit(b + C::TSZ, tid);
     if (tid < BQ) {
       stat[buf][0][tid] = st_lse;
       stat[buf][1][tid] = st_d;
@@ -238,57 +204,56 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const float c2 = a.scale_log2;
   KvStep cur = first_from(a.n_items - 1);
   if (cur.item >= 0) {
-    gload(cur);
-    sstore(0);
+    stage(cur, 0);
+    commit(0);
   }
+  wait_staged();
   __syncthreads();
   int buf = 0;
   while (cur.item >= 0) {
     const KvStep nxt = advance(cur);
-    if (nxt.item >= 0) gload(nxt);
-    const int32_t *it = a.items + cur.item * kItemWords;
+    if (nxt.item >= 0) stage(nxt, buf ^ 1);
+    const int32_t *it = items + cur.item * kItemWords;
     const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
     const int qt0 = cur.qt0;
     const int qt1 = min(qt0 + BQ, q_hi);
     if (has_keys && kw0 < qt1) {
-      const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + ROWS, *Qt = Qs + 2 * ROWS, *dOt = Qt + TRANS;
-      // ---- S = Q K^T and dP = dO V^T.  Query pair qp covers rows
-      // 32qp..32qp+31; half ab reads row 8*(m/4) + 4*ab + m%4 so a lane's 8
-      // values of a pair are the rows 32qp + 8*lg + 0..7 of its key.
-      f32x4 s[2][2][2], dp[2][2][2];
+      const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;
+      const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
+      // The 64 query rows are handled as two pairs of 32 (qp), one after the
+      // other, to bound the live score registers.
 #pragma unroll
-      for (int qp = 0; qp < 2; ++qp)
+      for (int qp = 0; qp < 2; ++qp) {
+        // ---- S = Q K^T and dP = dO V^T.  Half ab reads query row
+        // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of the pair are
+        // the rows 32qp + 8*lg + 0..7 for its key 16nk + l16.
+        f32x4 s[2][2], dp[2][2];
 #pragma unroll
         for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
           for (int nk = 0; nk < 2; ++nk) {
-            s[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            dp[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            s[ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            dp[ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int qp = 0; qp < 2; ++qp)
+        for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
             const int row = 32 * qp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(Qs + row * C::ROW + 32 * ks + 8 * lg);
-            const bf16x8 da = *reinterpret_cast<const bf16x8 *>(dOs + row * C::ROW + 32 * ks + 8 * lg);
+            const bf16x8 qa = tile_row8<D>(Qs, row, 32 * ks + 8 * lg);
+            const bf16x8 da = tile_row8<D>(dOs, row, 32 * ks + 8 * lg);
 #pragma unroll
             for (int nk = 0; nk < 2; ++nk) {
-              s[qp][ab][nk] = mfma16(qa, kf[nk][ks], s[qp][ab][nk]);
-              dp[qp][ab][nk] = mfma16(da, vf[nk][ks], dp[qp][ab][nk]);
+              s[ab][nk] = mfma16(qa, kf[nk][ks], s[ab][nk]);
+              dp[ab][nk] = mfma16(da, vf[nk][ks], dp[ab][nk]);
             }
           }
-      // ---- P and dS (lane: key 16nk + l16, rows 32qp + 8lg + j)
-      const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
-      bf16x8 pa[2][2], dsa[2][2];
-#pragma unroll
-      for (int qp = 0; qp < 2; ++qp) {
+        // ---- P and dS
         const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
         const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
         const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
         const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
+        bf16x8 pa[2], dsa[2];
 #pragma unroll
         for (int nk = 0; nk < 2; ++nk) {
           const int key = kw0 + 16 * nk + l16;
@@ -299,33 +264,32 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
             for (int i = 0; i < 4; ++i) {
               const float lq = ab ? l1[i] : l0[i];
               const float dq = ab ? d1[i] : d0[i];
-              float pv = fast_exp2(fmaf(s[qp][ab][nk][i], c2, -lq));
+              float pv = fast_exp2(fmaf(s[ab][nk][i], c2, -lq));
               if (need_mask) {
                 const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
                 if (key > q || key < k_lo || key >= k_hi) pv = 0.f;
               }
               p[ab][i] = pv;
-              ds[ab][i] = pv * (dp[qp][ab][nk][i] - dq);
+              ds[ab][i] = pv * (dp[ab][nk][i] - dq);
             }
-          pa[qp][nk] = pack_bf16x8(p[0], p[1]);
-          dsa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
+          pa[nk] = pack_bf16x8(p[0], p[1]);
+          dsa[nk] = pack_bf16x8(ds[0], ds[1]);
         }
-      }
-      // ---- dV += P^T dO, dK += dS^T Q  (B operands from the transposed tiles)
+        // ---- dV += P^T dO, dK += dS^T Q  (B operands read transposed from LDS)
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-        for (int qp = 0; qp < 2; ++qp) {
-          const bf16x8 dob = *reinterpret_cast<const bf16x8 *>(dOt + (16 * nt + l16) * C::TROW + 32 * qp + 8 * lg);
-          const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(Qt + (16 * nt + l16) * C::TROW + 32 * qp + 8 * lg);
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const bf16x8 dob = tile_rows8<D>(dOs, 32 * qp, 16 * nt, l16, lg);
+          const bf16x8 qb = tile_rows8<D>(Qs, 32 * qp, 16 * nt, l16, lg);
 #pragma unroll
           for (int nk = 0; nk < 2; ++nk) {
-            dv[nk][nt] = mfma16(pa[qp][nk], dob, dv[nk][nt]);
-            dk[nk][nt] = mfma16(dsa[qp][nk], qb, dk[nk][nt]);
+            dv[nk][nt] = mfma16(pa[nk], dob, dv[nk][nt]);
+            dk[nk][nt] = mfma16(dsa[nk], qb, dk[nk][nt]);
           }
         }
+      }
     }
-    if (nxt.item >= 0) sstore(buf ^ 1);
+    if (nxt.item >= 0) commit(buf ^ 1);
+    wait_staged();
     __syncthreads();
     cur = nxt;
     buf ^= 1;
@@ -340,7 +304,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int key = kw0 + 16 * nk + 4 * lg + i;
       if (has_keys && key < kt1) {
-        const int64_t base = ((int64_t)(seq_off + key) * a.hkv + g) * D + l16;
+        const int64_t base = ((int64_t)(seq_off + key) * hkv + g) * D + l16;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
           put1<GT>(dkg + base + 16 * nt, dk[nk][nt][i] * a.scale, a.accumulate);
@@ -361,8 +325,7 @@ template <int D, typename InT, typename GT>
 __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int BN = kBwdQBN;  // 64 keys per tile
-  constexpr int ROWS = BN * C::ROW, TRANS = D * C::TROW;
-  constexpr int BUF = 2 * ROWS + TRANS;  // K, V row-major + K transposed
+  constexpr int BUF = 2 * C::TSZ;  // K tile, V tile
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -370,13 +333,17 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 
   int rank, h;
   map_head(blockIdx.x, a.hq, rank, h);
+  const int32_t *__restrict__ items = a.items;
+  const float *__restrict__ lse = a.lse;
+  const float *__restrict__ delta = a.delta;
+  const int hq = a.hq, hkv = a.hkv;
   const int32_t *grp = a.qg + find_unit(a.qg, 4, 2, a.n_qg, rank) * 4;
   const int first = grp[0], count = grp[1];
-  const int32_t *it0 = a.items + first * kItemWords;
+  const int32_t *it0 = items + first * kItemWords;
   const int seq_off = it0[0], q_lo = it0[1], q_hi = it0[2];
   const int r1 = q_hi - (rank - grp[2]) * kBwdQBM;
   const int r0 = max(q_lo, r1 - kBwdQBM);
-  const int g = h / (a.hq / a.hkv);
+  const int g = h / (hq / hkv);
   const int64_t T = a.tokens;
   const InT *qg = static_cast<const InT *>(a.q);
   const InT *kg = static_cast<const InT *>(a.k);
@@ -394,15 +361,15 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const int row = rw0 + 16 * nq + l16;
     const bool ok = has_rows && row < r1;
     const int64_t grow = (int64_t)seq_off + (ok ? row : r0);
-    const int64_t base = (grow * a.hq + h) * D + 8 * lg;
+    const int64_t base = (grow * hq + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       qf[nq][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(qg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
       dof[nq][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(dg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
     }
-    const float l = ok ? a.lse[(int64_t)h * T + grow] : kNegInf;
+    const float l = ok ? lse[(int64_t)h * T + grow] : kNegInf;
     lse2[nq] = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    drow[nq] = ok ? a.delta[(int64_t)h * T + grow] : 0.f;
+    drow[nq] = ok ? delta[(int64_t)h * T + grow] : 0.f;
   }
 
   f32x4 dq[2][C::NT];
@@ -412,46 +379,49 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     for (int nt = 0; nt < C::NT; ++nt) dq[nq][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   // ---- step iterator over (item of the group in reverse order, key tile)
-  auto item_end = [&](int i) { return min(a.items[i * kItemWords + 4], r1); };
-  auto first_from = [&](int i) -> QStep {
+  auto item_end = [&](int i) __attribute__((always_inline)) { return min(items[i * kItemWords + 4], r1); };
+  auto first_from = [&](int i) __attribute__((always_inline)) -> QStep {
     for (; i >= first; --i)
-      if (item_end(i) > a.items[i * kItemWords + 3]) return QStep{i, a.items[i * kItemWords + 3]};
+      if (item_end(i) > items[i * kItemWords + 3]) return QStep{i, items[i * kItemWords + 3]};
     return QStep{-1, 0};
   };
-  auto advance = [&](QStep s) -> QStep {
+  auto advance = [&](QStep s) __attribute__((always_inline)) -> QStep {
     s.kv0 += BN;
     if (s.kv0 < item_end(s.item)) return s;
     return first_from(s.item - 1);
   };
 
-  TileStager<D, InT> sk, sv;
-  auto gload = [&](const QStep &s) {
+  TileLoader<D, InT> lk, lv;
+  const int64_t kstride = (int64_t)hkv * D;
+  auto stage = [&](const QStep &s, int buf) __attribute__((always_inline)) {
     const int nvalid = min(BN, item_end(s.item) - s.kv0);
-    const int64_t row0 = (int64_t)seq_off + s.kv0;
-    sk.load(kg, row0, nvalid, a.hkv, g, tid);
-    sv.load(vg, row0, nvalid, a.hkv, g, tid);
-  };
-  auto sstore = [&](int buf) {
+    const int64_t off = (((int64_t)seq_off + s.kv0) * hkv + g) * D;
     __bf16 *b = lds + buf * BUF;
-    sk.store(b, b + 2 * ROWS, tid);
-    sv.store(b + ROWS, nullptr, tid);
+    lk.issue(b, kg + off, kstride, nvalid, wave, lane);
+    lv.issue(b + C::TSZ, vg + off, kstride, nvalid, wave, lane);
+  };
+  auto commit = [&](int buf) __attribute__((always_inline)) {
+    __bf16 *b = lds + buf * BUF;
+    lk.commit(b, tid);
+    lv.commit(b + C::TSZ, tid);
   };
 
   const float c2 = a.scale_log2;
   QStep cur = first_from(first + count - 1);
   if (cur.item >= 0) {
-    gload(cur);
-    sstore(0);
+    stage(cur, 0);
+    commit(0);
   }
+  wait_staged();
   __syncthreads();
   int buf = 0;
   while (cur.item >= 0) {
     const QStep nxt = advance(cur);
-    if (nxt.item >= 0) gload(nxt);
+    if (nxt.item >= 0) stage(nxt, buf ^ 1);
     const int kv0 = cur.kv0;
-    const int k_hi = a.items[cur.item * kItemWords + 4];
+    const int k_hi = items[cur.item * kItemWords + 4];
     if (has_rows && kv0 <= rw_end - 1) {
-      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + ROWS, *Kt = Ks + 2 * ROWS;
+      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ;
       // ---- S^T = K Q^T, dP^T = V dO^T (key pair kp, half ab as in the forward)
       f32x4 s[2][2][2], dp[2][2][2];
 #pragma unroll
@@ -470,8 +440,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
             const int kvr = 32 * kp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Ks + kvr * C::ROW + 32 * ks + 8 * lg);
-            const bf16x8 va = *reinterpret_cast<const bf16x8 *>(Vs + kvr * C::ROW + 32 * ks + 8 * lg);
+            const bf16x8 ka = tile_row8<D>(Ks, kvr, 32 * ks + 8 * lg);
+            const bf16x8 va = tile_row8<D>(Vs, kvr, 32 * ks + 8 * lg);
 #pragma unroll
             for (int nq = 0; nq < 2; ++nq) {
               s[nq][kp][ab] = mfma16(ka, qf[nq][ks], s[nq][kp][ab]);
@@ -505,12 +475,13 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
       for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kt + (16 * nt + l16) * C::TROW + 32 * kp + 8 * lg);
+          const bf16x8 ka = tile_rows8<D>(Ks, 32 * kp, 16 * nt, l16, lg);
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka, dsb[nq][kp], dq[nq][nt]);
         }
     }
-    if (nxt.item >= 0) sstore(buf ^ 1);
+    if (nxt.item >= 0) commit(buf ^ 1);
+    wait_staged();
     __syncthreads();
     cur = nxt;
     buf ^= 1;
@@ -522,7 +493,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   for (int nq = 0; nq < 2; ++nq) {
     const int row = rw0 + 16 * nq + l16;
     if (has_rows && row < r1) {
-      GT *p = dqg + (((int64_t)seq_off + row) * a.hq + h) * D + 4 * lg;
+      GT *p = dqg + (((int64_t)seq_off + row) * hq + h) * D + 4 * lg;
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) put4<GT>(p + 16 * nt, dq[nq][nt] * a.scale, a.accumulate);
     }

@@ -20,6 +20,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -56,6 +59,19 @@ __device__ __forceinline__ u32x4 load8<float>(const float *p) {
   const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
   return (u32x4){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
                  pack_bf16x2(b[2], b[3])};
+}
+
+// Operand of a contraction over ROWS of a row-major bf16 LDS tile: lane l
+// receives tile[row0 + 8*(l/16) + j][col0 + l%16], j = 0..7 (the A layout
+// with m = column, k = row; equally the B layout with n = column).
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
+// 8 bytes loaded by lane 4k + i/4 as its k-th value, so lane j points at
+// row 8*(l/16) + j/4, columns 4*(j%4) .. +3.  Needs col0 % 4 == 0.
+__device__ __forceinline__ bf16x8 lds_rows8(const __bf16 *tile, int stride, int row0, int col0, int l16, int lg) {
+  const __bf16 *p = tile + (row0 + 8 * lg + (l16 >> 2)) * stride + col0 + 4 * (l16 & 3);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * stride));
+  return __builtin_bit_cast(bf16x8, (s16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
 // Byte-select of two dwords: result byte i = byte sel_i of {hi:lo}.

@@ -2,8 +2,8 @@
 //
 // One workgroup = one query tile of up to 256 rows of one work item and one
 // query head (4 waves x 64 rows).  The item's visible keys are streamed in
-// 64-key tiles staged through LDS (K row-major, V transposed, double
-// buffered) while the query rows stay in registers.  Scores are computed
+// 64-key tiles staged row-major through LDS (double buffered) while the
+// query rows stay in registers.  Scores are computed
 // transposed, S^T = K Q^T, so that every lane owns one query row's scores:
 // the row max and the row sum of the online softmax then need only two
 // cross-lane steps, and the probabilities are already in the B-operand layout
@@ -17,6 +17,7 @@
 // optionally merged into an existing fp32 (O, LSE) with the log-sum-exp rule.
 #include "device_common.h"
 #include "kernels.h"
+#include "tile.h"
 
 namespace segattn {
 namespace dev {
@@ -24,19 +25,15 @@ namespace dev {
 template <int D>
 struct FwdCfg {
   static constexpr int BM = kFwdBM;        // query rows per workgroup
-  static constexpr int BN = kFwdBN;        // keys per LDS tile
+  static constexpr int BN = kFwdBN;        // keys per LDS tile (= kTileRows)
   static constexpr int NQ = 4;             // 16-row subtiles per wave (64 rows)
   static constexpr int KS = D / 32;        // depth steps of K Q^T
   static constexpr int MT = D / 16;        // 16-wide head-dim tiles of O^T
   static constexpr int KP = BN / 32;       // 32-key pairs per tile
-  static constexpr int KROW = D + 8;       // LDS K row stride (bf16)
-  static constexpr int VROW = BN + 8;      // LDS V^T row stride (bf16)
-  static constexpr int KSZ = BN * KROW;
-  static constexpr int VSZ = D * VROW;
-  static constexpr int BUF = KSZ + VSZ;
-  static constexpr int KCH = BN * D / 8 / 256;    // 16-byte K chunks per thread
-  static constexpr int VBLK = (BN / 4) * (D / 8); // 4-key x 8-dim V blocks
+  static constexpr int TSZ = BN * D;       // one swizzled tile (bf16 elements)
+  static constexpr int BUF = 2 * TSZ;      // K tile, V tile
 };
+static_assert(kFwdBN == kTileRows, "forward key tile is one LDS tile");
 
 // Workgroup index -> (tile rank, head).  Consecutive workgroups go to the 8
 // XCDs in turn; when hq is a multiple of 8, XCD c gets the heads
@@ -133,66 +130,35 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // Global -> register staging of one K/V tile starting at key kvs.
-  u32x4 kreg[C::KCH], vreg[4];
-  auto gload = [&](int kvs) {
-#pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + 256 * r, row = c / (D / 8), cc = c % (D / 8);
-      const int kr = kvs + row;
-      kreg[r] = kr < ke ? load8<InT>(kg + ((int64_t)(seq_off + kr) * a.hkv + g) * D + 8 * cc)
-                        : (u32x4){0, 0, 0, 0};
-    }
-    if (tid < C::VBLK) {
-      const int kvq = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = kvs + 4 * kvq + r;
-        vreg[r] = kr < ke ? load8<InT>(vg + ((int64_t)(seq_off + kr) * a.hkv + g) * D + 8 * dc)
-                          : (u32x4){0, 0, 0, 0};
-      }
-    }
-  };
-  // Register -> LDS: K row-major, V transposed (V^T[d][key]).
-  auto sstore = [&](int buf) {
+  // K and V tiles of 64 keys starting at key kvs, staged into LDS buffer buf.
+  TileLoader<D, InT> lk, lv;
+  const int64_t kvstride = (int64_t)a.hkv * D;
+  auto stage = [&](int kvs, int buf) {
     __bf16 *Ks = lds + buf * C::BUF;
-    __bf16 *Vt = Ks + C::KSZ;
-#pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + 256 * r, row = c / (D / 8), cc = c % (D / 8);
-      *reinterpret_cast<u32x4 *>(Ks + row * C::KROW + 8 * cc) = kreg[r];
-    }
-    if (tid < C::VBLK) {
-      const int kvq = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        u32x2 pk;
-        if (dd & 1) {
-          pk[0] = join_hi(vreg[0][w], vreg[1][w]);
-          pk[1] = join_hi(vreg[2][w], vreg[3][w]);
-        } else {
-          pk[0] = join_lo(vreg[0][w], vreg[1][w]);
-          pk[1] = join_lo(vreg[2][w], vreg[3][w]);
-        }
-        *reinterpret_cast<u32x2 *>(Vt + (8 * dc + dd) * C::VROW + 4 * kvq) = pk;
-      }
-    }
+    const int64_t off = ((int64_t)(seq_off + kvs) * a.hkv + g) * D;
+    lk.issue(Ks, kg + off, kvstride, ke - kvs, wave, lane);
+    lv.issue(Ks + C::TSZ, vg + off, kvstride, ke - kvs, wave, lane);
+  };
+  auto commit = [&](int buf) {
+    __bf16 *Ks = lds + buf * C::BUF;
+    lk.commit(Ks, tid);
+    lv.commit(Ks + C::TSZ, tid);
   };
 
   const float c2 = a.scale_log2;
 
   if (ntiles > 0) {
-    gload(kb);
-    sstore(0);
+    stage(kb, 0);
+    commit(0);
   }
+  wait_staged();
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = kb + j * C::BN;
-    if (j + 1 < ntiles) gload(kv0 + C::BN);
+    if (j + 1 < ntiles) stage(kv0 + C::BN, (j + 1) & 1);
     const __bf16 *Ks = lds + (j & 1) * C::BUF;
-    const __bf16 *Vt = Ks + C::KSZ;
+    const __bf16 *Vs = Ks + C::TSZ;
 
     if (has_rows && kv0 <= rw_max) {
       // ---- S^T = K Q^T.  Pair kp covers keys 32kp..32kp+31; half ab of the
@@ -213,7 +179,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
             const int kvr = 32 * kp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + kvr * C::KROW + 32 * ks + 8 * lg);
+            const bf16x8 kf = tile_row8<D>(Ks, kvr, 32 * ks + 8 * lg);
 #pragma unroll
             for (int nq = 0; nq < C::NQ; ++nq) s[nq][kp][ab] = mfma16(kf, qf[nq][ks], s[nq][kp][ab]);
           }
@@ -240,10 +206,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
               }
               mx = fmaxf(mx, val);
             }
-        mx = wave_max_xor16_32(mx);
-        const float m_new = fmaxf(m_run[nq], mx * c2);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[nq] - m_use);
+        mx = wave_max_xor16_32(mx) * c2;
+        // Lazy rescale: the running maximum m_run only moves when a row's
+        // maximum exceeds it by more than 8 (so every p <= 2^8); softmax is
+        // invariant to the shift, and the final 1/l and LSE use the same m.
+        const bool grow = mx > m_run[nq] + 8.f;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run[nq];
+          const float alpha = grow ? fast_exp2(m_run[nq] - m_new) : 1.f;  // m_run = -inf -> 0
+          l_run[nq] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] *= alpha;
+          m_run[nq] = m_new;
+        }
+        const float m_use = m_run[nq] == kNegInf ? 0.f : m_run[nq];
         float rs = 0.f;
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp)
@@ -255,10 +231,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
               s[nq][kp][ab][i] = p;
               rs += p;
             }
-        l_run[nq] = fmaf(l_run[nq], alpha, rs);
-        m_run[nq] = m_new;
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] *= alpha;
+        l_run[nq] += rs;
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp) pf[nq][kp] = pack_bf16x8(s[nq][kp][0], s[nq][kp][1]);
       }
@@ -268,14 +241,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8 *>(Vt + (16 * mt + l16) * C::VROW + 32 * kp + 8 * lg);
+          const bf16x8 vf = tile_rows8<D>(Vs, 32 * kp, 16 * mt, l16, lg);
 #pragma unroll
           for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf, pf[nq][kp], o[nq][mt]);
         }
     }
 
-    if (j + 1 < ntiles) sstore((j + 1) & 1);
+    if (j + 1 < ntiles) commit((j + 1) & 1);
+    wait_staged();
     __syncthreads();
   }
 
