@@ -11,16 +11,23 @@
 // over the items in REVERSE item order, so no atomics are needed and the
 // result is deterministic.
 //
-// dkdv_kernel: key-stationary.  A workgroup owns 128 keys of one KV head
-//   (4 waves x 32 keys; K and V in registers) and walks every (item, query
+// dkdv_kernel: key-stationary.  A workgroup owns 128 keys of one KV head in
+//   4 groups of 32; each group is handled by two wavefronts on one SIMD, one
+//   accumulating dV, the other dK (K, and for dK also V, in registers).  It
+//   walks every (item, query
 //   head of the group, 64-row query tile) that can see them; per tile it
-//   recomputes S, P, dP, dS and accumulates dV and dK (4 products).  Q and
-//   dO tiles are staged row-major; the operands contracted over query rows
-//   are read with transposing LDS reads.
-// dq_kernel: query-stationary, like the forward.  A workgroup owns 128 query
-//   rows of one head (4 waves x 32 rows; Q and dO in registers) and walks the
+//   recomputes S and P (both roles) and dP, dS (dK role) and accumulates dV
+//   and dK: 5 products, one more than strictly needed, so that each role
+//   fits in half a SIMD's registers and two wavefronts share every SIMD.  Q
+//   and dO tiles are staged row-major; the operands contracted over query
+//   rows are read with transposing LDS reads.
+// dq_kernel: query-stationary, like the forward.  A workgroup owns 256 query
+//   rows of one head (8 waves x 32 rows, two per SIMD; Q and dO in registers)
+//   and walks the
 //   64-key tiles of every item of its query group; per tile it recomputes
 //   S^T, P, dP^T, dS^T and accumulates dQ^T (3 products).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tile.h"
@@ -91,16 +98,43 @@ struct KvStep {
   int qt0;   // first query row of the tile (sequence-local)
 };
 
+// Next step at or below item i: the first item (walking down) of sequence
+// seq_off whose keys meet [kt0, kt1) and whose queries reach past kt0.
+__device__ __forceinline__ KvStep kv_first_from(const int32_t *items, int i, int seq_off, int kt0, int kt1) {
+  for (; i >= 0; --i) {
+    const int32_t *it = items + i * kItemWords;
+    if (it[0] == seq_off && it[3] < kt1 && it[4] > kt0 && it[2] > kt0) return KvStep{i, 0, max(it[1], kt0)};
+  }
+  return KvStep{-1, 0, 0};
+}
+
+__device__ __forceinline__ KvStep kv_advance(const int32_t *items, KvStep s, int G, int seq_off, int kt0, int kt1) {
+  const int32_t *it = items + s.item * kItemWords;
+  s.qt0 += kBwdKvBM;
+  if (s.qt0 < it[2]) return s;
+  if (++s.hh < G) {
+    s.qt0 = max(it[1], kt0);
+    return s;
+  }
+  return kv_first_from(items, s.item - 1, seq_off, kt0, kt1);
+}
+
 template <int D, typename InT, typename GT>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  constexpr int BQ = kBwdKvBM;  // 64 query rows per tile
-  constexpr int BUF = 2 * C::TSZ;  // Q tile, dO tile
+  constexpr int W = kBwdKvWaves;
+  constexpr int BQ = kBwdKvBM;     // 64 query rows per tile
+  constexpr int BUF = 4 * C::TSZ;  // Q, dO as row tiles, then Q, dO as column tiles
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];  // [buf][lse2 | D][row]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
+  // Wavefronts w and w + W/2 share key group w % (W/2) (and a SIMD): the
+  // first accumulates dV (needs P), the second dK (needs P and dP).
+  const int kgrp = wave % (W / 2);
+  const bool dk_role = wave >= W / 2;
 
   int rank, g;
   map_head(blockIdx.x, a.hkv, rank, g);
@@ -119,12 +153,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const InT *vg = static_cast<const InT *>(a.v);
   const InT *dg = static_cast<const InT *>(a.d_o);
 
-  // This wave's keys [kw0, kw0 + 32).
-  const int kw0 = kt0 + 32 * wave;
+  // This wavefront's keys [kw0, kw0 + 32).
+  const int kw0 = kt0 + 32 * kgrp;
   const bool has_keys = kw0 < kt1;
 
-  // K and V fragments (B operands of Q K^T and dO V^T): lane holds
-  // K[key = kw0 + 16nk + l16][32ks + 8lg .. +8].
+  // K fragments (B operand of Q K^T), and for the dK role V fragments
+  // (B operand of dO V^T): lane holds X[key = kw0 + 16nk + l16][32ks + 8lg ..].
   bf16x8 kf[2][C::KS], vf[2][C::KS];
 #pragma unroll
   for (int nk = 0; nk < 2; ++nk) {
@@ -134,97 +168,87 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       kf[nk][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(kg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
-      vf[nk][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(vg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
+      vf[nk][ks] = __builtin_bit_cast(bf16x8, ok && dk_role ? load8<InT>(vg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
     }
   }
 
-  f32x4 dk[2][C::NT], dv[2][C::NT];
+  // dV (first role) or dK (second role) accumulator.
+  f32x4 acc[2][C::NT];
 #pragma unroll
   for (int nk = 0; nk < 2; ++nk)
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-      dk[nk][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      dv[nk][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nt = 0; nt < C::NT; ++nt) acc[nk][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // ---- step iterator over (item in reverse order, head, query tile)
-  auto item_sees = [&](int i) __attribute__((always_inline)) {
-    const int32_t *it = items + i * kItemWords;
-    return it[0] == seq_off && it[3] < kt1 && it[4] > kt0 && it[2] > kt0;
-  };
-  auto first_from = [&](int i) __attribute__((always_inline)) -> KvStep {
-    for (; i >= 0; --i)
-      if (item_sees(i)) return KvStep{i, 0, max(items[i * kItemWords + 1], kt0)};
-    return KvStep{-1, 0, 0};
-  };
-  auto advance = [&](KvStep s) __attribute__((always_inline)) -> KvStep {
-    const int32_t *it = items + s.item * kItemWords;
-    s.qt0 += BQ;
-    if (s.qt0 < it[2]) return s;
-    if (++s.hh < G) {
-      s.qt0 = max(it[1], kt0);
-      return s;
-    }
-    return first_from(s.item - 1);
-  };
+  // Loop-invariant LDS byte offsets of this lane's reads.
+  int roff[C::KS], coff[C::NT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(ks, l16, lg);
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
 
-  TileLoader<D, InT> lq, ldo;
-  float st_lse = 0.f, st_d = 0.f;
   const int64_t qstride = (int64_t)hq * D;
-  auto stage = [&](const KvStep &s, int buf) __attribute__((always_inline)) {
+  TileLoader<D, InT, W> lqd;  // Q and dO tiles: same rows and stride
+  lqd.init(wave, lane, qstride);
+  // Staged per-row statistics (base-2 LSE and D) of one query tile; only the
+  // first BQ threads hold one row each.
+  struct RowStat {
+    float lse2, d;
+  };
+  auto stage = [&](const KvStep &s, int buf) __attribute__((always_inline)) -> RowStat {
     const int32_t *it = items + s.item * kItemWords;
     const int h = g * G + s.hh;
     const int nvalid = min(BQ, it[2] - s.qt0);
     const int64_t row0 = (int64_t)seq_off + s.qt0;
     __bf16 *b = lds + buf * BUF;
-    lq.issue(b, qg + (row0 * hq + h) * D, qstride, nvalid, wave, lane);
-    ldo.issue(b + C::TSZ, dg + (row0 * hq + h) * D, qstride, nvalid, wave, lane);
-    if (tid < BQ) {
-      if (tid < nvalid) {
-        const float l = lse[(int64_t)h * T + row0 + tid];
-        // A row without visible keys (LSE = -inf) contributes nothing.
-        st_lse = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        st_d = delta[(int64_t)h * T + row0 + tid];
-      } else {
-        st_lse = __builtin_inff();
-        st_d = 0.f;
-      }
+    const InT *qs = qg + (row0 * hq + h) * D, *ds = dg + (row0 * hq + h) * D;
+    lqd.template issue<kRowTile>(b, qs, nvalid, wave, 0);
+    lqd.template issue<kRowTile>(b + C::TSZ, ds, nvalid, wave, 1);
+    lqd.template issue<kColTile>(b + 2 * C::TSZ, qs, nvalid, wave, 0);
+    lqd.template issue<kColTile>(b + 3 * C::TSZ, ds, nvalid, wave, 1);
+    RowStat st{__builtin_inff(), 0.f};
+    if (tid < nvalid) {
+      const float l = lse[(int64_t)h * T + row0 + tid];
+      // A row without visible keys (LSE = -inf) contributes nothing.
+      st.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+      st.d = delta[(int64_t)h * T + row0 + tid];
     }
+    return st;
   };
-  auto commit = [&](int buf) __attribute__((always_inline)) {
+  auto commit = [&](int buf, RowStat st) __attribute__((always_inline)) {
     __bf16 *b = lds + buf * BUF;
-    lq.commit(b, tid);
-    ldo.commit(b + C::TSZ, tid);
+    lqd.template commit<kRowTile>(b, tid, 0);
+    lqd.template commit<kRowTile>(b + C::TSZ, tid, 1);
+    lqd.template commit<kColTile>(b + 2 * C::TSZ, tid, 0);
+    lqd.template commit<kColTile>(b + 3 * C::TSZ, tid, 1);
     if (tid < BQ) {
-      stat[buf][0][tid] = st_lse;
-      stat[buf][1][tid] = st_d;
+      stat[buf][0][tid] = st.lse2;
+      stat[buf][1][tid] = st.d;
     }
   };
 
   const float c2 = a.scale_log2;
-  KvStep cur = first_from(a.n_items - 1);
-  if (cur.item >= 0) {
-    stage(cur, 0);
-    commit(0);
-  }
+  KvStep cur = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
+  if (cur.item >= 0) commit(0, stage(cur, 0));
   wait_staged();
   __syncthreads();
-  int buf = 0;
-  while (cur.item >= 0) {
-    const KvStep nxt = advance(cur);
-    if (nxt.item >= 0) stage(nxt, buf ^ 1);
+  // One query tile; the LDS buffer index is a compile-time constant so every
+  // LDS read is a precomputed lane offset plus an immediate.
+  auto step = [&](const KvStep cur, auto bufc) __attribute__((always_inline)) -> KvStep {
+    constexpr int buf = decltype(bufc)::value;
+    const KvStep nxt = kv_advance(items, cur, G, seq_off, kt0, kt1);
+    RowStat nst{0.f, 0.f};
+    if (nxt.item >= 0) nst = stage(nxt, buf ^ 1);
     const int32_t *it = items + cur.item * kItemWords;
     const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
     const int qt0 = cur.qt0;
     const int qt1 = min(qt0 + BQ, q_hi);
     if (has_keys && kw0 < qt1) {
-      const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;
+      const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;          // row tiles
+      const __bf16 *Qc = Qs + 2 * C::TSZ, *dOc = Qs + 3 * C::TSZ;     // column tiles
       const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
-      // The 64 query rows are handled as two pairs of 32 (qp), one after the
-      // other, to bound the live score registers.
 #pragma unroll
       for (int qp = 0; qp < 2; ++qp) {
-        // ---- S = Q K^T and dP = dO V^T.  Half ab reads query row
+        // ---- S = Q K^T (and dP = dO V^T for dK).  Half ab reads query row
         // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of the pair are
         // the rows 32qp + 8*lg + 0..7 for its key 16nk + l16.
         f32x4 s[2][2], dp[2][2];
@@ -239,65 +263,65 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
-            const int row = 32 * qp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 qa = tile_row8<D>(Qs, row, 32 * ks + 8 * lg);
-            const bf16x8 da = tile_row8<D>(dOs, row, 32 * ks + 8 * lg);
+            const bf16x8 qa = lds_row8(Qs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
 #pragma unroll
-            for (int nk = 0; nk < 2; ++nk) {
-              s[ab][nk] = mfma16(qa, kf[nk][ks], s[ab][nk]);
-              dp[ab][nk] = mfma16(da, vf[nk][ks], dp[ab][nk]);
+            for (int nk = 0; nk < 2; ++nk) s[ab][nk] = mfma16(qa, kf[nk][ks], s[ab][nk]);
+            if (dk_role) {
+              const bf16x8 da = lds_row8(dOs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+#pragma unroll
+              for (int nk = 0; nk < 2; ++nk) dp[ab][nk] = mfma16(da, vf[nk][ks], dp[ab][nk]);
             }
           }
-        // ---- P and dS
+        // ---- P (dV role) or dS = P (dP - D) (dK role), packed as the A operand
         const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
         const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
-        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
-        bf16x8 pa[2], dsa[2];
+        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        if (dk_role) {
+          d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
+          d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
+        }
+        bf16x8 opa[2];
 #pragma unroll
         for (int nk = 0; nk < 2; ++nk) {
           const int key = kw0 + 16 * nk + l16;
-          f32x4 p[2], ds[2];
+          f32x4 x[2];
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float lq = ab ? l1[i] : l0[i];
-              const float dq = ab ? d1[i] : d0[i];
               float pv = fast_exp2(fmaf(s[ab][nk][i], c2, -lq));
               if (need_mask) {
                 const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
                 if (key > q || key < k_lo || key >= k_hi) pv = 0.f;
               }
-              p[ab][i] = pv;
-              ds[ab][i] = pv * (dp[ab][nk][i] - dq);
+              x[ab][i] = dk_role ? pv * (dp[ab][nk][i] - (ab ? d1[i] : d0[i])) : pv;
             }
-          pa[nk] = pack_bf16x8(p[0], p[1]);
-          dsa[nk] = pack_bf16x8(ds[0], ds[1]);
+          opa[nk] = pack_bf16x8(x[0], x[1]);
         }
-        // ---- dV += P^T dO, dK += dS^T Q  (B operands read transposed from LDS)
+        // ---- dV += P^T dO or dK += dS^T Q (B operand read transposed from LDS)
+        const __bf16 *Bt = dk_role ? Qc : dOc;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          const bf16x8 dob = tile_rows8<D>(dOs, 32 * qp, 16 * nt, l16, lg);
-          const bf16x8 qb = tile_rows8<D>(Qs, 32 * qp, 16 * nt, l16, lg);
+          const bf16x8 bt = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) {
-            dv[nk][nt] = mfma16(pa[nk], dob, dv[nk][nt]);
-            dk[nk][nt] = mfma16(dsa[nk], qb, dk[nk][nt]);
-          }
+          for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[nk], bt, acc[nk][nt]);
         }
       }
     }
-    if (nxt.item >= 0) commit(buf ^ 1);
+    if (nxt.item >= 0) commit(buf ^ 1, nst);
     wait_staged();
     __syncthreads();
-    cur = nxt;
-    buf ^= 1;
+    return nxt;
+  };
+  while (cur.item >= 0) {
+    cur = step(cur, std::integral_constant<int, 0>{});
+    if (cur.item >= 0) cur = step(cur, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: lane holds rows key = kw0 + 16nk + 4lg + i, column 16nt + l16
-  GT *dkg = static_cast<GT *>(a.dk);
-  GT *dvg = static_cast<GT *>(a.dv);
+  GT *outg = static_cast<GT *>(dk_role ? a.dk : a.dv);
+  const float osc = dk_role ? a.scale : 1.f;
 #pragma unroll
   for (int nk = 0; nk < 2; ++nk)
 #pragma unroll
@@ -306,10 +330,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       if (has_keys && key < kt1) {
         const int64_t base = ((int64_t)(seq_off + key) * hkv + g) * D + l16;
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-          put1<GT>(dkg + base + 16 * nt, dk[nk][nt][i] * a.scale, a.accumulate);
-          put1<GT>(dvg + base + 16 * nt, dv[nk][nt][i], a.accumulate);
-        }
+        for (int nt = 0; nt < C::NT; ++nt) put1<GT>(outg + base + 16 * nt, acc[nk][nt][i] * osc, a.accumulate);
       }
     }
 }
@@ -321,14 +342,31 @@ struct QStep {
   int kv0;
 };
 
+// Next step at or below item i of a query group (items first..): the first
+// item (walking down) with a key inside [k_lo, min(k_hi, r1)).
+__device__ __forceinline__ QStep q_first_from(const int32_t *items, int i, int first, int r1) {
+  for (; i >= first; --i) {
+    const int32_t *it = items + i * kItemWords;
+    if (min(it[4], r1) > it[3]) return QStep{i, it[3]};
+  }
+  return QStep{-1, 0};
+}
+
+__device__ __forceinline__ QStep q_advance(const int32_t *items, QStep s, int first, int r1) {
+  s.kv0 += kBwdQBN;
+  if (s.kv0 < min(items[s.item * kItemWords + 4], r1)) return s;
+  return q_first_from(items, s.item - 1, first, r1);
+}
+
 template <int D, typename InT, typename GT>
-__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int BN = kBwdQBN;  // 64 keys per tile
-  constexpr int BUF = 2 * C::TSZ;  // K tile, V tile
+  constexpr int BUF = 3 * C::TSZ;  // K and V as row tiles, K as a column tile
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
 
   int rank, h;
@@ -378,94 +416,90 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) dq[nq][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // ---- step iterator over (item of the group in reverse order, key tile)
   auto item_end = [&](int i) __attribute__((always_inline)) { return min(items[i * kItemWords + 4], r1); };
-  auto first_from = [&](int i) __attribute__((always_inline)) -> QStep {
-    for (; i >= first; --i)
-      if (item_end(i) > items[i * kItemWords + 3]) return QStep{i, items[i * kItemWords + 3]};
-    return QStep{-1, 0};
-  };
-  auto advance = [&](QStep s) __attribute__((always_inline)) -> QStep {
-    s.kv0 += BN;
-    if (s.kv0 < item_end(s.item)) return s;
-    return first_from(s.item - 1);
-  };
 
-  TileLoader<D, InT> lk, lv;
+  // Loop-invariant LDS byte offsets of this lane's reads.
+  int roff[C::KS], coff[C::NT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(ks, l16, lg);
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
+
   const int64_t kstride = (int64_t)hkv * D;
+  TileLoader<D, InT, kBwdQWaves> lkv;  // K and V tiles: same rows and stride
+  lkv.init(wave, lane, kstride);
   auto stage = [&](const QStep &s, int buf) __attribute__((always_inline)) {
     const int nvalid = min(BN, item_end(s.item) - s.kv0);
     const int64_t off = (((int64_t)seq_off + s.kv0) * hkv + g) * D;
     __bf16 *b = lds + buf * BUF;
-    lk.issue(b, kg + off, kstride, nvalid, wave, lane);
-    lv.issue(b + C::TSZ, vg + off, kstride, nvalid, wave, lane);
+    lkv.template issue<kRowTile>(b, kg + off, nvalid, wave, 0);
+    lkv.template issue<kRowTile>(b + C::TSZ, vg + off, nvalid, wave, 1);
+    lkv.template issue<kColTile>(b + 2 * C::TSZ, kg + off, nvalid, wave, 0);
   };
   auto commit = [&](int buf) __attribute__((always_inline)) {
     __bf16 *b = lds + buf * BUF;
-    lk.commit(b, tid);
-    lv.commit(b + C::TSZ, tid);
+    lkv.template commit<kRowTile>(b, tid, 0);
+    lkv.template commit<kRowTile>(b + C::TSZ, tid, 1);
+    lkv.template commit<kColTile>(b + 2 * C::TSZ, tid, 0);
   };
 
   const float c2 = a.scale_log2;
-  QStep cur = first_from(first + count - 1);
+  QStep cur = q_first_from(items, first + count - 1, first, r1);
   if (cur.item >= 0) {
     stage(cur, 0);
     commit(0);
   }
   wait_staged();
   __syncthreads();
-  int buf = 0;
-  while (cur.item >= 0) {
-    const QStep nxt = advance(cur);
+  auto step = [&](const QStep cur, auto bufc) __attribute__((always_inline)) -> QStep {
+    constexpr int buf = decltype(bufc)::value;
+    const QStep nxt = q_advance(items, cur, first, r1);
     if (nxt.item >= 0) stage(nxt, buf ^ 1);
     const int kv0 = cur.kv0;
     const int k_hi = items[cur.item * kItemWords + 4];
     if (has_rows && kv0 <= rw_end - 1) {
-      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ;
-      // ---- S^T = K Q^T, dP^T = V dO^T (key pair kp, half ab as in the forward)
-      f32x4 s[2][2][2], dp[2][2][2];
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq)
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            s[nq][kp][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            dp[nq][kp][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            const int kvr = 32 * kp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 ka = tile_row8<D>(Ks, kvr, 32 * ks + 8 * lg);
-            const bf16x8 va = tile_row8<D>(Vs, kvr, 32 * ks + 8 * lg);
-#pragma unroll
-            for (int nq = 0; nq < 2; ++nq) {
-              s[nq][kp][ab] = mfma16(ka, qf[nq][ks], s[nq][kp][ab]);
-              dp[nq][kp][ab] = mfma16(va, dof[nq][ks], dp[nq][kp][ab]);
-            }
-          }
+      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ, *Kc = Ks + 2 * C::TSZ;
       const bool need_mask = (kv0 + BN - 1 > rw0) || (kv0 + BN > k_hi);
       bf16x8 dsb[2][2];
+      // Each 32-key pair kp is finished (scores -> dS) before the next one
+      // starts, which bounds the live score registers.
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-        const int qrow = rw0 + 16 * nq + l16;
+      for (int kp = 0; kp < 2; ++kp) {
+        // ---- S^T = K Q^T, dP^T = V dO^T (half ab as in the forward)
+        f32x4 s[2][2], dp[2][2];
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
+        for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab) {
+            s[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            dp[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab) {
+            const bf16x8 ka = lds_row8(Ks, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
+            const bf16x8 va = lds_row8(Vs, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
+#pragma unroll
+            for (int nq = 0; nq < 2; ++nq) {
+              s[nq][ab] = mfma16(ka, qf[nq][ks], s[nq][ab]);
+              dp[nq][ab] = mfma16(va, dof[nq][ks], dp[nq][ab]);
+            }
+          }
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) {
+          const int qrow = rw0 + 16 * nq + l16;
           f32x4 ds[2];
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float pv = fast_exp2(fmaf(s[nq][kp][ab][i], c2, -lse2[nq]));
+              float pv = fast_exp2(fmaf(s[nq][ab][i], c2, -lse2[nq]));
               if (need_mask) {
                 const int key = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
                 if (key > qrow || key >= k_hi) pv = 0.f;
               }
-              ds[ab][i] = pv * (dp[nq][kp][ab][i] - drow[nq]);
+              ds[ab][i] = pv * (dp[nq][ab][i] - drow[nq]);
             }
           dsb[nq][kp] = pack_bf16x8(ds[0], ds[1]);
         }
@@ -475,7 +509,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
       for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          const bf16x8 ka = tile_rows8<D>(Ks, 32 * kp, 16 * nt, l16, lg);
+          const bf16x8 ka = lds_col8<D>(Kc, coff[nt] + 32 * kp * 2 * D);
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka, dsb[nq][kp], dq[nq][nt]);
         }
@@ -483,8 +517,11 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     if (nxt.item >= 0) commit(buf ^ 1);
     wait_staged();
     __syncthreads();
-    cur = nxt;
-    buf ^= 1;
+    return nxt;
+  };
+  while (cur.item >= 0) {
+    cur = step(cur, std::integral_constant<int, 0>{});
+    if (cur.item >= 0) cur = step(cur, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: lane holds dQ[row = rw0 + 16nq + l16][16nt + 4lg + i]
@@ -503,14 +540,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 template <int D, typename InT, typename GT>
 static hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_kv_units * a.hkv;
-  hipLaunchKernelGGL((dkdv_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((dkdv_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, typename InT, typename GT>
 static hipError_t launch_dq_t(const BwdArgs &a, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_q_units * a.hq;
-  hipLaunchKernelGGL((dq_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((dq_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdQWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,14 +83,24 @@ __device__ __forceinline__ uint32_t join_lo(uint32_t x, uint32_t y) { return per
 // high bf16 of x and high bf16 of y -> (y.hi << 16) | x.hi
 __device__ __forceinline__ uint32_t join_hi(uint32_t x, uint32_t y) { return perm(y, x, 0x07060302u); }
 
-__device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
+// Byte addresses for ds_bpermute of lane ^ 16 and lane ^ 32 (computed once).
+struct XorLanes {
+  int x16, x32;
+  __device__ __forceinline__ XorLanes(int lane) : x16((lane ^ 16) << 2), x32((lane ^ 32) << 2) {}
+};
+__device__ __forceinline__ float bperm(int addr, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+// Reductions over the lanes l, l^16, l^32, l^48 (the 4 lane groups that hold
+// one row's scores).
+__device__ __forceinline__ float wave_max_xor16_32(float v, const XorLanes &x) {
+  v = fmaxf(v, bperm(x.x16, v));
+  v = fmaxf(v, bperm(x.x32, v));
   return v;
 }
-__device__ __forceinline__ float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
+__device__ __forceinline__ float wave_sum_xor16_32(float v, const XorLanes &x) {
+  v += bperm(x.x16, v);
+  v += bperm(x.x32, v);
   return v;
 }
 

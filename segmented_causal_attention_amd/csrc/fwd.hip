@@ -1,13 +1,15 @@
 // Forward partial attention kernel for gfx950 (CDNA4), bf16 MFMA.
 //
 // One workgroup = one query tile of up to 256 rows of one work item and one
-// query head (4 waves x 64 rows).  The item's visible keys are streamed in
-// 64-key tiles staged row-major through LDS (double buffered) while the
-// query rows stay in registers.  Scores are computed
-// transposed, S^T = K Q^T, so that every lane owns one query row's scores:
-// the row max and the row sum of the online softmax then need only two
-// cross-lane steps, and the probabilities are already in the B-operand layout
-// of the second product O^T += V^T P^T.
+// query head: 8 wavefronts x 32 rows, two wavefronts per SIMD, so one
+// wavefront's softmax overlaps the other's matrix products.  The item's
+// visible keys are streamed in 64-key tiles that global_load_lds copies
+// straight into swizzled LDS tiles (double buffered) while the query rows stay
+// in registers.  Scores are computed transposed, S^T = K Q^T, so that every
+// lane owns one query row's scores: the row max needs only two cross-lane
+// steps, and the probabilities are already in the B-operand layout of the
+// second product O^T += V^T P^T, whose V^T operand comes from transposing LDS
+// reads.
 //
 // What it computes (SPPO section 5.1 / Figure 9: a segment's queries against
 // the resident K/V of all segments up to it; InfiniPipe section II-A: one
@@ -15,6 +17,8 @@
 // item, over the visible keys j (k_lo <= j < k_hi, j <= q),
 //   LSE_q = log sum_j exp(scale <Q_q, K_j>),   O_q = sum_j exp(scale <Q_q,K_j> - LSE_q) V_j,
 // optionally merged into an existing fp32 (O, LSE) with the log-sum-exp rule.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tile.h"
@@ -24,16 +28,17 @@ namespace dev {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = kFwdBM;        // query rows per workgroup
+  static constexpr int W = kFwdWaves;      // wavefronts per workgroup
+  static constexpr int BM = kFwdBM;        // query rows per workgroup (W x 32)
   static constexpr int BN = kFwdBN;        // keys per LDS tile (= kTileRows)
-  static constexpr int NQ = 4;             // 16-row subtiles per wave (64 rows)
+  static constexpr int NQ = 2;             // 16-row subtiles per wavefront (32 rows)
   static constexpr int KS = D / 32;        // depth steps of K Q^T
   static constexpr int MT = D / 16;        // 16-wide head-dim tiles of O^T
   static constexpr int KP = BN / 32;       // 32-key pairs per tile
   static constexpr int TSZ = BN * D;       // one swizzled tile (bf16 elements)
-  static constexpr int BUF = 2 * TSZ;      // K tile, V tile
+  static constexpr int BUF = 2 * TSZ;      // K (row tile), V (column tile)
 };
-static_assert(kFwdBN == kTileRows, "forward key tile is one LDS tile");
+static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * 32, "forward tile shape");
 
 // Workgroup index -> (tile rank, head).  Consecutive workgroups go to the 8
 // XCDs in turn; when hq is a multiple of 8, XCD c gets the heads
@@ -75,12 +80,14 @@ __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x4 &v) {
 }
 
 template <int D, typename InT, typename OutT>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
+  const XorLanes xl(lane);
 
   int rank, h;
   map_unit(blockIdx.x, a.hq, rank, h);
@@ -89,32 +96,41 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int tile = rank - it[5];
   const int r1 = q_hi - tile * C::BM;             // heaviest (last) rows first
   const int r0 = max(q_lo, r1 - C::BM);
-  const int g = (h * a.hkv) / a.hq;
+  const int hq = a.hq, hkv = a.hkv;
+  const int g = (h * hkv) / hq;
   const int64_t T = a.tokens;
 
   const InT *__restrict__ qg = static_cast<const InT *>(a.q);
   const InT *__restrict__ kg = static_cast<const InT *>(a.k);
   const InT *__restrict__ vg = static_cast<const InT *>(a.v);
 
-  // This wave's query rows [rw0, rw_end).
-  const int rw0 = r0 + 64 * wave;
-  const int rw_end = min(rw0 + 64, r1);
+  // This wavefront's query rows [rw0, rw_end).
+  const int rw0 = r0 + 32 * wave;
+  const int rw_end = min(rw0 + 32, r1);
   const bool has_rows = rw0 < rw_end;
   const int rw_max = rw_end - 1;
 
-  // Query fragments (B operand of K Q^T): lane holds Q[row = l16][8*lg .. +8].
+  // Query fragments (B operand of K Q^T): lane holds Q[row = l16][8*lg .. +8]
+  // of each 32-dim step, matching the K row reads of logical chunk 4ks + lg.
   bf16x8 qf[C::NQ][C::KS];
 #pragma unroll
   for (int nq = 0; nq < C::NQ; ++nq) {
     const int row = rw0 + 16 * nq + l16;
     const bool ok = has_rows && row < r1;
-    const InT *qp = qg + ((int64_t)(seq_off + (ok ? row : r0)) * a.hq + h) * D + 8 * lg;
+    const InT *qp = qg + ((int64_t)(seq_off + (ok ? row : r0)) * hq + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 w = ok ? load8<InT>(qp + 32 * ks) : (u32x4){0, 0, 0, 0};
       qf[nq][ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
+
+  // Loop-invariant LDS byte offsets of this lane's reads.
+  int roff[C::KS], coff[C::MT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(ks, l16, lg);
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) coff[mt] = col_read_off<D>(mt, l16, lg);
 
   const int kb = k_lo;
   const int ke = min(k_hi, r1);
@@ -131,33 +147,30 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   }
 
   // K and V tiles of 64 keys starting at key kvs, staged into LDS buffer buf.
-  TileLoader<D, InT> lk, lv;
-  const int64_t kvstride = (int64_t)a.hkv * D;
-  auto stage = [&](int kvs, int buf) {
+  const int64_t kvstride = (int64_t)hkv * D;
+  TileLoader<D, InT, C::W> lkv;
+  lkv.init(wave, lane, kvstride);
+  auto stage = [&](int kvs, int buf) __attribute__((always_inline)) {
     __bf16 *Ks = lds + buf * C::BUF;
-    const int64_t off = ((int64_t)(seq_off + kvs) * a.hkv + g) * D;
-    lk.issue(Ks, kg + off, kvstride, ke - kvs, wave, lane);
-    lv.issue(Ks + C::TSZ, vg + off, kvstride, ke - kvs, wave, lane);
+    const int64_t off = ((int64_t)(seq_off + kvs) * hkv + g) * D;
+    lkv.template issue<kRowTile>(Ks, kg + off, ke - kvs, wave, 0);
+    lkv.template issue<kColTile>(Ks + C::TSZ, vg + off, ke - kvs, wave, 1);
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf) __attribute__((always_inline)) {
     __bf16 *Ks = lds + buf * C::BUF;
-    lk.commit(Ks, tid);
-    lv.commit(Ks + C::TSZ, tid);
+    lkv.template commit<kRowTile>(Ks, tid, 0);
+    lkv.template commit<kColTile>(Ks + C::TSZ, tid, 1);
   };
 
   const float c2 = a.scale_log2;
 
-  if (ntiles > 0) {
-    stage(kb, 0);
-    commit(0);
-  }
-  wait_staged();
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
+  // One key tile: the LDS buffer index is a compile-time constant so every
+  // LDS read is a precomputed lane offset plus an immediate.
+  auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int kv0 = kb + j * C::BN;
-    if (j + 1 < ntiles) stage(kv0 + C::BN, (j + 1) & 1);
-    const __bf16 *Ks = lds + (j & 1) * C::BUF;
+    if (j + 1 < ntiles) stage(kv0 + C::BN, buf ^ 1);
+    const __bf16 *Ks = lds + buf * C::BUF;
     const __bf16 *Vs = Ks + C::TSZ;
 
     if (has_rows && kv0 <= rw_max) {
@@ -178,8 +191,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
-            const int kvr = 32 * kp + 8 * (l16 >> 2) + 4 * ab + (l16 & 3);
-            const bf16x8 kf = tile_row8<D>(Ks, kvr, 32 * ks + 8 * lg);
+            const bf16x8 kf = lds_row8(Ks, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
 #pragma unroll
             for (int nq = 0; nq < C::NQ; ++nq) s[nq][kp][ab] = mfma16(kf, qf[nq][ks], s[nq][kp][ab]);
           }
@@ -206,7 +218,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
               }
               mx = fmaxf(mx, val);
             }
-        mx = wave_max_xor16_32(mx) * c2;
+        mx = wave_max_xor16_32(mx, xl) * c2;
         // Lazy rescale: the running maximum m_run only moves when a row's
         // maximum exceeds it by more than 8 (so every p <= 2^8); softmax is
         // invariant to the shift, and the final 1/l and LSE use the same m.
@@ -241,22 +253,33 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp) {
-          const bf16x8 vf = tile_rows8<D>(Vs, 32 * kp, 16 * mt, l16, lg);
+          const bf16x8 vf = lds_col8<D>(Vs, coff[mt] + 32 * kp * 2 * D);
 #pragma unroll
           for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf, pf[nq][kp], o[nq][mt]);
         }
     }
 
-    if (j + 1 < ntiles) commit((j + 1) & 1);
+    if (j + 1 < ntiles) commit(buf ^ 1);
     wait_staged();
     __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    stage(kb, 0);
+    commit(0);
+  }
+  wait_staged();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: normalise, optional merge, write O rows and LSE.
   OutT *__restrict__ og = static_cast<OutT *>(a.o);
 #pragma unroll
   for (int nq = 0; nq < C::NQ; ++nq) {
-    const float lt = wave_sum_xor16_32(l_run[nq]);
+    const float lt = wave_sum_xor16_32(l_run[nq], xl);
     const int qrow = rw0 + 16 * nq + l16;
     const bool valid = has_rows && qrow < r1;
     const float lse_new = lt > 0.f ? (m_run[nq] + fast_log2(lt)) * kLn2 : kNegInf;
@@ -278,7 +301,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     }
     if (valid) {
-      OutT *op = og + (grow * a.hq + h) * D + 4 * lg;
+      OutT *op = og + (grow * hq + h) * D + 4 * lg;
       const float sc = inv * w_new;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 template <int D, typename InT, typename OutT>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_units * a.hq;
-  hipLaunchKernelGGL((fwd_kernel<D, InT, OutT>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, InT, OutT>), dim3((unsigned)grid), dim3(64 * FwdCfg<D>::W), 0, s, a);
   return hipGetLastError();
 }
 

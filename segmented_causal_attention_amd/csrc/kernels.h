@@ -15,19 +15,23 @@ namespace segattn {
 //   [6] aux0  [7] aux1  (per-kernel meaning, see below)
 constexpr int kItemWords = 8;
 
-// Forward tile shape: 256 query rows per workgroup (4 waves x 64 rows),
+// Forward tile shape: kFwdWaves wavefronts x 32 query rows per workgroup,
 // 64 keys per K/V tile staged through LDS.
-constexpr int kFwdBM = 256;
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBM = 32 * kFwdWaves;
 constexpr int kFwdBN = 64;
 
 // Backward tile shapes.
-//   dK/dV kernel: 128 keys per workgroup (4 waves x 32 keys), 64 query rows
-//                 per staged Q/dO tile.
-//   dQ kernel:    128 query rows per workgroup (4 waves x 32 rows), 64 keys
+//   dK/dV kernel: 128 keys per workgroup (4 key groups x 32 keys, each with
+//                 a dV wavefront and a dK wavefront), 64 query rows per
+//                 staged Q/dO tile.
+//   dQ kernel:    256 query rows per workgroup (8 waves x 32 rows), 64 keys
 //                 per staged K/V tile.
-constexpr int kBwdKvBN = 128;
+constexpr int kBwdKvWaves = 8;
+constexpr int kBwdKvBN = 32 * (kBwdKvWaves / 2);
 constexpr int kBwdKvBM = 64;
-constexpr int kBwdQBM = 128;
+constexpr int kBwdQWaves = 8;
+constexpr int kBwdQBM = 32 * kBwdQWaves;
 constexpr int kBwdQBN = 64;
 
 struct FwdArgs {

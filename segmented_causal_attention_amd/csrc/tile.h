@@ -1,14 +1,25 @@
 // 64-row bf16 tiles in LDS shared by the forward and backward kernels.
 //
-// Layout: row-major, D columns, no padding.  The 16-byte chunk c of row r is
-// stored at chunk position c ^ swz(r).  The swizzle spreads, over the 32 LDS
-// banks, both read patterns the kernels use:
-//   * 16-byte row reads (MFMA operands contracted over the head dim) whose
-//     16 lanes visit rows 8a + b (a, b = 0..3): swz takes each value twice;
-//   * 8-byte transposing reads (operands contracted over rows) whose 16 lanes
-//     visit rows 8*lg + b.
-// Without padding a wavefront can fill 1 KB of a tile with one
+// Layout: row-major, D columns, no padding; the 16-byte chunk c of row r is
+// stored at chunk position c ^ swz<KIND>(r).  gfx950's LDS has 64 four-byte
+// banks (a 256-byte row of a D = 128 tile spans all of them), and each tile is
+// stored in the layout that suits the way the kernels read it:
+//   KIND 0 (row tiles) -- 16-byte row reads of MFMA operands contracted over
+//     the head dim; lanes visit rows 8a + b (a, b = 0..3) at one logical
+//     chunk.  swz = (r & 3) | ((r >> 3) & 3) << 2.
+//   KIND 1 (column tiles) -- 8-byte transposing reads of operands contracted
+//     over rows; each half-wavefront visits rows 8g + b of g in {0,1} (or
+//     {2,3}), two chunks each, and needs eight disjoint 32-byte bank windows.
+//     swz = ((r >> 3) & 1) << 3 | (r & 3) << 1 | (r >> 4) & 1.
+// Both were measured bank-conflict free on the device (SQ_LDS_BANK_CONFLICT);
+// each is 2-way conflicted under the other access, so a tensor read both ways
+// is staged twice.  For D = 64 (8 chunks per row) the swizzle is taken mod 8.
+// Without padding a wavefront fills 1 KB of a tile with one
 // global_load_lds_dwordx4 (global memory straight to LDS, no registers).
+//
+// The per-lane byte offsets of every read are loop invariant; kernels compute
+// them once (row_read_off / col_read_off) and add compile-time immediates for
+// the pair, half and buffer indices (the swizzles ignore row bits 2 and 5).
 #pragma once
 
 #include "device_common.h"
@@ -18,81 +29,137 @@ namespace dev {
 
 constexpr int kTileRows = 64;
 
-__device__ __forceinline__ int swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+constexpr int kRowTile = 0;  // read with 16-byte row reads
+constexpr int kColTile = 1;  // read with 8-byte transposing reads
 
-// Element offset of (row r, column col) in a swizzled tile; col % 4 == 0.
-template <int D>
-__device__ __forceinline__ int toff(int r, int col) {
-  return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+template <int D, int KIND>
+__device__ __forceinline__ int swz(int r) {
+  const int f = KIND == kRowTile ? ((r & 3) | (((r >> 3) & 3) << 2))
+                                 : ((((r >> 3) & 1) << 3) | ((r & 3) << 1) | ((r >> 4) & 1));
+  return f & (D / 8 - 1);
 }
 
-// 16-byte read: tile[r][col .. col+7] (col % 8 == 0).
+// Byte offset, inside a tile of the given kind, of the 16-byte chunk c of row r.
+template <int D, int KIND>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return r * (2 * D) + ((c ^ swz<D, KIND>(r)) << 4);
+}
+
+// Row reads.  Lane (l16, lg) of step ks reads 8 consecutive columns of row
+// rho(l16) = 8*(l16/4) + l16%4 (plus a multiple of 4 rows added as an
+// immediate, which leaves f unchanged) at logical chunk 4*ks + lg.
+// Returns the byte offset for step ks.
 template <int D>
-__device__ __forceinline__ bf16x8 tile_row8(const __bf16 *t, int r, int col) {
-  return *reinterpret_cast<const bf16x8 *>(t + toff<D>(r, col));
+__device__ __forceinline__ int row_read_off(int ks, int l16, int lg) {
+  const int r = 8 * (l16 >> 2) + (l16 & 3);
+  return chunk_off<D, kRowTile>(r, 4 * ks + lg);
+}
+
+// Transposing reads.  For column block mt (16 columns) lane (l16, lg) points
+// at row 8*lg + l16/4 (plus multiples of 4 rows as immediates), columns
+// 16*mt + 4*(l16%4) .. +3.  Returns the byte offset.
+template <int D>
+__device__ __forceinline__ int col_read_off(int mt, int l16, int lg) {
+  const int r = 8 * lg + (l16 >> 2);
+  const int c = 2 * mt + ((l16 & 3) >> 1);
+  return chunk_off<D, kColTile>(r, c) + 8 * (l16 & 1);
+}
+
+__device__ __forceinline__ const char *lds_at(const void *base, int byte_off) {
+  return static_cast<const char *>(base) + byte_off;
+}
+
+// 16-byte row read at a precomputed byte offset.
+__device__ __forceinline__ bf16x8 lds_row8(const void *base, int byte_off) {
+  return *reinterpret_cast<const bf16x8 *>(lds_at(base, byte_off));
 }
 
 // Operand of a contraction over ROWS: lane l receives
-// tile[row0 + 8*(l/16) + j][col0 + l%16], j = 0..7.  ds_read_b64_tr_b16
-// hands lane i of each 16-lane group element i%4 of the 8 bytes loaded by
-// lane 4k + i/4 as its k-th value, so lane j points at row
-// row0 + 8*(l/16) + j/4, columns col0 + 4*(j%4) .. +3 (col0 % 16 == 0).
+// tile[row0 + 8*(l/16) + j][16*mt + l%16], j = 0..7, given
+// off = col_read_off(mt) + row0 * 2D.  ds_read_b64_tr_b16 hands lane i of
+// each 16-lane group element i%4 of the 8 bytes loaded by lane 4k + i/4 as
+// its k-th value; the second read covers rows +4.
 template <int D>
-__device__ __forceinline__ bf16x8 tile_rows8(const __bf16 *t, int row0, int col0, int l16, int lg) {
-  const int r = row0 + 8 * lg + (l16 >> 2), c = col0 + 4 * (l16 & 3);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff<D>(r, c)));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff<D>(r + 4, c)));
+__device__ __forceinline__ bf16x8 lds_col8(const void *base, int byte_off) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)lds_at(base, byte_off));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)lds_at(base, byte_off + 4 * 2 * D));
   return __builtin_bit_cast(bf16x8, (s16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
-// Stages a 64-row tile of a token-major tensor into LDS.  Rows >= nvalid
-// are filled from row nvalid-1 (bf16 path) or with zeros (fp32 path); the
-// kernels mask them, they only need to be finite.
-//   src: first row of the tile; stride: elements between consecutive rows.
-// bf16: issue() starts direct global->LDS copies (each of the 4 waves copies
-//   16 rows); the caller waits for them (vmcnt) before the barrier that
-//   publishes the tile.  commit() does nothing.
-// fp32: issue() loads into registers, commit() rounds to bf16 and stores.
-template <int D, typename InT>
+// Stages 64-row tiles of a token-major tensor into LDS with W wavefronts.
+// Rows >= nvalid are filled from row nvalid-1 (bf16 path) or with zeros
+// (fp32 path); the kernels mask them, they only need to be finite.
+//   init(): stride = elements between consecutive rows of the tensor;
+//   issue<KIND>(): src = first row of the tile; KIND = tile layout.
+// bf16: issue() starts direct global->LDS copies; the caller waits for them
+//   (wait_staged) before the barrier that publishes the tile.  commit() does
+//   nothing.
+// fp32: issue() loads into a register slot, commit() rounds to bf16 and
+//   stores (used only for fp32 inputs; one loader stages two tensors).
+template <int D, typename InT, int W>
 struct TileLoader;
 
-template <int D>
-struct TileLoader<D, __bf16> {
-  static constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;  // rows per wavefront instruction
-  __device__ __forceinline__ void issue(__bf16 *tile, const __bf16 *src, int64_t stride, int nvalid, int wave,
-                                        int lane) {
+template <int D, int W>
+struct TileLoader<D, __bf16, W> {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;           // rows per wavefront instruction
+  static constexpr int NI = kTileRows / RPI / W;  // instructions per wavefront
+  static_assert(NI >= 1 && NI * RPI * W == kTileRows, "tile split");
+  int row_[NI];     // lane's tile row per instruction
+  int off_[2][NI];  // element offset of the lane's chunk in a full tile, per tile kind
+  int stride_;      // elements between rows (< 2^31 / 64 is checked on the host)
+  int wave_;        // wavefront index (scalar)
+  __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
+    stride_ = (int)stride;
+    wave_ = wave;
 #pragma unroll
-    for (int t = 0; t < 16 / RPI; ++t) {
-      const int rb = wave * 16 + t * RPI;  // first row of this instruction (uniform)
-      const int r = rb + lane / CPR;
-      const int c = (lane % CPR) ^ swz(r);
-      const int gr = max(0, min(r, nvalid - 1));
-      __builtin_amdgcn_global_load_lds((const void *)(src + gr * stride + 8 * c),
-                                       (__attribute__((address_space(3))) void *)(tile + rb * D), 16, 0, 0);
+    for (int t = 0; t < NI; ++t) {
+      row_[t] = (wave * NI + t) * RPI + lane / CPR;
+      off_[kRowTile][t] = row_[t] * stride_ + 8 * ((lane % CPR) ^ swz<D, kRowTile>(row_[t]));
+      off_[kColTile][t] = row_[t] * stride_ + 8 * ((lane % CPR) ^ swz<D, kColTile>(row_[t]));
     }
   }
-  __device__ __forceinline__ void commit(__bf16 *, int) const {}
+  template <int KIND>
+  __device__ __forceinline__ void issue(__bf16 *tile, const __bf16 *src, int nvalid, int, int = 0) const {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      int off = off_[KIND][t];
+      if (nvalid < kTileRows && row_[t] >= nvalid)  // partial tile: repeat the last valid row
+        off += (nvalid - 1 - row_[t]) * stride_;
+      __builtin_amdgcn_global_load_lds((const void *)(src + off),
+                                       (__attribute__((address_space(3))) void *)(tile + (wave_ * NI + t) * RPI * D),
+                                       16, 0, 0);
+    }
+  }
+  template <int KIND>
+  __device__ __forceinline__ void commit(__bf16 *, int, int = 0) const {}
 };
 
-template <int D>
-struct TileLoader<D, float> {
+template <int D, int W>
+struct TileLoader<D, float, W> {
   static constexpr int CPR = D / 8;
-  static constexpr int N = 64 * CPR / 256;  // chunks per thread
-  u32x4 r_[N];
-  __device__ __forceinline__ void issue(__bf16 *, const float *src, int64_t stride, int nvalid, int wave, int lane) {
-    const int tid = wave * 64 + lane;
+  static constexpr int N = (kTileRows * CPR + 64 * W - 1) / (64 * W);  // chunks per thread
+  u32x4 r_[2][N];  // two staged tensors (slot 0 / 1)
+  int64_t stride_;
+  __device__ __forceinline__ void init(int, int, int64_t stride) { stride_ = stride; }
+  // fp32 path: issue<KIND>(...) loads into register slot `slot` (the tile
+  // pointer is unused until commit).
+  template <int KIND>
+  __device__ __forceinline__ void issue(__bf16 *, const float *src, int nvalid, int wave, int slot = 0) {
+    const int tid = wave * 64 + (int)(threadIdx.x & 63);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int ch = tid + 256 * i, row = ch / CPR, c = ch % CPR;
-      r_[i] = row < nvalid ? load8<float>(src + row * stride + 8 * c) : (u32x4){0, 0, 0, 0};
+      const int ch = tid + 64 * W * i, row = ch / CPR, c = ch % CPR;
+      r_[slot][i] = (row < kTileRows && row < nvalid) ? load8<float>(src + row * stride_ + 8 * c) : (u32x4){0, 0, 0, 0};
     }
   }
-  __device__ __forceinline__ void commit(__bf16 *tile, int tid) const {
+  template <int KIND>
+  __device__ __forceinline__ void commit(__bf16 *tile, int tid, int slot = 0) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int ch = tid + 256 * i, row = ch / CPR, c = ch % CPR;
-      *reinterpret_cast<u32x4 *>(tile + toff<D>(row, 8 * c)) = r_[i];
+      const int ch = tid + 64 * W * i, row = ch / CPR, c = ch % CPR;
+      if (row < kTileRows)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(tile) + chunk_off<D, KIND>(row, c)) = r_[slot][i];
     }
   }
 };
