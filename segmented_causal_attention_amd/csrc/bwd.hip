@@ -12,13 +12,14 @@
 // result is deterministic.
 //
 // dkdv_kernel: key-stationary.  A workgroup owns 128 keys of one KV head in
-//   4 groups of 32; each group is handled by two wavefronts on one SIMD, one
-//   accumulating dV, the other dK (K, and for dK also V, in registers).  It
-//   walks every (item, query
-//   head of the group, 64-row query tile) that can see them; per tile it
-//   recomputes S and P (both roles) and dP, dS (dK role) and accumulates dV
-//   and dK: 5 products, one more than strictly needed, so that each role
-//   fits in half a SIMD's registers and two wavefronts share every SIMD.  Q
+//   4 groups of 32; each group is handled by two wavefronts on one SIMD.  It
+//   walks every (item, query head of the group, 64-row query tile) that can
+//   see its keys.  Per tile, the dV wavefront computes S = Q K^T and P and
+//   hands P (fp16) to the dK wavefront through LDS while that one computes
+//   dP = dO V^T; after a barrier the first accumulates dV += P^T dO, the
+//   second dS = P (dP - D) and dK += dS^T Q.  Each wavefront keeps only its
+//   own key-side operand (K or V) and accumulator in registers, so two fit
+//   on every SIMD, and the two do equal MFMA work (4 products per tile).  Q
 //   and dO tiles are staged row-major; the operands contracted over query
 //   rows are read with transposing LDS reads.
 // dq_kernel: query-stationary, like the forward.  A workgroup owns 256 query
@@ -123,18 +124,23 @@ template <int D, typename InT, typename GT>
 __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int W = kBwdKvWaves;
+  constexpr int NG = W / 2;        // key groups of 32 keys
   constexpr int BQ = kBwdKvBM;     // 64 query rows per tile
   constexpr int BUF = 4 * C::TSZ;  // Q, dO as row tiles, then Q, dO as column tiles
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];  // [buf][lse2 | D][row]
+  // P of the current tile, handed from each group's dV wavefront to its dK
+  // wavefront: [group][32-row half][16-key block][lane] x 8 fp16 values.
+  __shared__ __attribute__((aligned(16))) uint32_t pshare[NG][2][2][64][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  // Wavefronts w and w + W/2 share key group w % (W/2) (and a SIMD): the
-  // first accumulates dV (needs P), the second dK (needs P and dP).
-  const int kgrp = wave % (W / 2);
-  const bool dk_role = wave >= W / 2;
+  // Wavefronts w and w + NG share key group w % NG (and a SIMD): the first
+  // computes P and accumulates dV, the second computes dP, takes P from the
+  // first through LDS, and accumulates dK.
+  const int kgrp = wave % NG;
+  const bool dk_role = wave >= NG;
 
   int rank, g;
   map_head(blockIdx.x, a.hkv, rank, g);
@@ -149,26 +155,26 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   const float *__restrict__ delta = a.delta;
   const int hq = a.hq, hkv = a.hkv;
   const InT *qg = static_cast<const InT *>(a.q);
-  const InT *kg = static_cast<const InT *>(a.k);
-  const InT *vg = static_cast<const InT *>(a.v);
   const InT *dg = static_cast<const InT *>(a.d_o);
 
   // This wavefront's keys [kw0, kw0 + 32).
   const int kw0 = kt0 + 32 * kgrp;
   const bool has_keys = kw0 < kt1;
 
-  // K fragments (B operand of Q K^T), and for the dK role V fragments
-  // (B operand of dO V^T): lane holds X[key = kw0 + 16nk + l16][32ks + 8lg ..].
-  bf16x8 kf[2][C::KS], vf[2][C::KS];
+  // Key-side fragments, B operand of the contraction over the head dim:
+  // K (dV role: S = Q K^T) or V (dK role: dP = dO V^T);
+  // lane holds X[key = kw0 + 16nk + l16][32ks + 8lg ..].
+  bf16x8 xf[2][C::KS];
+  {
+    const InT *xg = static_cast<const InT *>(dk_role ? a.v : a.k);
 #pragma unroll
-  for (int nk = 0; nk < 2; ++nk) {
-    const int key = kw0 + 16 * nk + l16;
-    const bool ok = key < kt1;
-    const int64_t base = ((int64_t)(seq_off + (ok ? key : kt0)) * hkv + g) * D + 8 * lg;
+    for (int nk = 0; nk < 2; ++nk) {
+      const int key = kw0 + 16 * nk + l16;
+      const bool ok = key < kt1;
+      const int64_t base = ((int64_t)(seq_off + (ok ? key : kt0)) * hkv + g) * D + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kf[nk][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(kg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
-      vf[nk][ks] = __builtin_bit_cast(bf16x8, ok && dk_role ? load8<InT>(vg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
+      for (int ks = 0; ks < C::KS; ++ks)
+        xf[nk][ks] = __builtin_bit_cast(bf16x8, ok ? load8<InT>(xg + base + 32 * ks) : (u32x4){0, 0, 0, 0});
     }
   }
 
@@ -231,8 +237,16 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   if (cur.item >= 0) commit(0, stage(cur, 0));
   wait_staged();
   __syncthreads();
-  // One query tile; the LDS buffer index is a compile-time constant so every
-  // LDS read is a precomputed lane offset plus an immediate.
+  // One query tile in two phases separated by a barrier:
+  //   A: dV role  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS (fp16);
+  //      dK role  dP = dO V^T.
+  //   B: dV role  dV += P^T dO;
+  //      dK role  dS = P (dP - D) with P from LDS, dK += dS^T Q.
+  // Rows: half qp, sub-block ab of a 32-row half reads query rows
+  // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of a half are the rows
+  // 32qp + 8*lg + 0..7 for its key 16nk + l16 -- the A operand layout of the
+  // contraction over query rows.  The LDS buffer index is a compile-time
+  // constant so every LDS read is a precomputed lane offset plus an immediate.
   auto step = [&](const KvStep cur, auto bufc) __attribute__((always_inline)) -> KvStep {
     constexpr int buf = decltype(bufc)::value;
     const KvStep nxt = kv_advance(items, cur, G, seq_off, kt0, kt1);
@@ -242,72 +256,91 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
     const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
     const int qt0 = cur.qt0;
     const int qt1 = min(qt0 + BQ, q_hi);
-    if (has_keys && kw0 < qt1) {
-      const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;          // row tiles
-      const __bf16 *Qc = Qs + 2 * C::TSZ, *dOc = Qs + 3 * C::TSZ;     // column tiles
-      const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
+    const bool active = has_keys && kw0 < qt1;
+    const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;       // row tiles
+    const __bf16 *Qc = Qs + 2 * C::TSZ, *dOc = Qs + 3 * C::TSZ;  // column tiles
+    const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows of the phase-A product
+    bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
+    f32x4 x[2][2][2];                       // [qp][ab][nk]: S or dP
+    // ---------------------------------------------------------- phase A
+    if (active) {
 #pragma unroll
-      for (int qp = 0; qp < 2; ++qp) {
-        // ---- S = Q K^T (and dP = dO V^T for dK).  Half ab reads query row
-        // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of the pair are
-        // the rows 32qp + 8*lg + 0..7 for its key 16nk + l16.
-        f32x4 s[2][2], dp[2][2];
+      for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
         for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) {
-            s[ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            dp[ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
-          }
+          for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
-            const bf16x8 qa = lds_row8(Qs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+            const bf16x8 xa = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
 #pragma unroll
-            for (int nk = 0; nk < 2; ++nk) s[ab][nk] = mfma16(qa, kf[nk][ks], s[ab][nk]);
-            if (dk_role) {
-              const bf16x8 da = lds_row8(dOs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
-#pragma unroll
-              for (int nk = 0; nk < 2; ++nk) dp[ab][nk] = mfma16(da, vf[nk][ks], dp[ab][nk]);
-            }
+            for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = mfma16(xa, xf[nk][ks], x[qp][ab][nk]);
           }
-        // ---- P (dV role) or dS = P (dP - D) (dK role), packed as the A operand
-        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
-        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-        if (dk_role) {
-          d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
-          d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
-        }
-        bf16x8 opa[2];
+      if (!dk_role) {
+        const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
 #pragma unroll
-        for (int nk = 0; nk < 2; ++nk) {
-          const int key = kw0 + 16 * nk + l16;
-          f32x4 x[2];
+        for (int qp = 0; qp < 2; ++qp) {
+          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
+          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab)
+          for (int nk = 0; nk < 2; ++nk) {
+            const int key = kw0 + 16 * nk + l16;
+            f32x4 pv[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float lq = ab ? l1[i] : l0[i];
-              float pv = fast_exp2(fmaf(s[ab][nk][i], c2, -lq));
-              if (need_mask) {
-                const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
-                if (key > q || key < k_lo || key >= k_hi) pv = 0.f;
+            for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, -(ab ? l1[i] : l0[i])));
+                if (need_mask) {
+                  const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
+                  if (key > q || key < k_lo || key >= k_hi) p = 0.f;
+                }
+                pv[ab][i] = p;
               }
-              x[ab][i] = dk_role ? pv * (dp[ab][nk][i] - (ab ? d1[i] : d0[i])) : pv;
-            }
-          opa[nk] = pack_bf16x8(x[0], x[1]);
+            opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
+            const u32x4 ph = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
+                              pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
+            *reinterpret_cast<u32x4 *>(pshare[kgrp][qp][nk][lane]) = ph;
+          }
         }
-        // ---- dV += P^T dO or dK += dS^T Q (B operand read transposed from LDS)
-        const __bf16 *Bt = dk_role ? Qc : dOc;
+      }
+    }
+    __syncthreads();
+    // ---------------------------------------------------------- phase B
+    if (active) {
+      if (dk_role) {
+#pragma unroll
+        for (int qp = 0; qp < 2; ++qp) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
+#pragma unroll
+          for (int nk = 0; nk < 2; ++nk) {
+            const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[kgrp][qp][nk][lane]);
+            f32x4 ds[2];
+#pragma unroll
+            for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = f16_at(ph[2 * ab + (i >> 1)], i & 1);
+                ds[ab][i] = p * (x[qp][ab][nk][i] - (ab ? d1[i] : d0[i]));
+              }
+            opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
+          }
+        }
+      }
+      const __bf16 *Bt = dk_role ? Qc : dOc;
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
           const bf16x8 bt = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[nk], bt, acc[nk][nt]);
+          for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt, acc[nk][nt]);
         }
-      }
     }
     if (nxt.item >= 0) commit(buf ^ 1, nst);
     wait_staged();
