@@ -282,31 +282,39 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
           }
       if (!dk_role) {
         const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
+        // The masked variant is a separate code path so that interior tiles
+        // carry no per-element compares.
+        auto make_p = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qp = 0; qp < 2; ++qp) {
-          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
-          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
+          for (int qp = 0; qp < 2; ++qp) {
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) {
-            const int key = kw0 + 16 * nk + l16;
-            f32x4 pv[2];
+            for (int nk = 0; nk < 2; ++nk) {
+              const int key = kw0 + 16 * nk + l16;
+              f32x4 pv[2];
 #pragma unroll
-            for (int ab = 0; ab < 2; ++ab)
+              for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, -(ab ? l1[i] : l0[i])));
-                if (need_mask) {
-                  const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
-                  if (key > q || key < k_lo || key >= k_hi) p = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                  float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, -(ab ? l1[i] : l0[i])));
+                  if constexpr (decltype(maskc)::value) {
+                    const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
+                    if (key > q || key < k_lo || key >= k_hi) p = 0.f;
+                  }
+                  pv[ab][i] = p;
                 }
-                pv[ab][i] = p;
-              }
-            opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
-            const u32x4 ph = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
-                              pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
-            *reinterpret_cast<u32x4 *>(pshare[kgrp][qp][nk][lane]) = ph;
+              opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
+              const u32x4 ph = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
+                                pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
+              *reinterpret_cast<u32x4 *>(pshare[kgrp][qp][nk][lane]) = ph;
+            }
           }
-        }
+        };
+        if (need_mask)
+          make_p(std::true_type{});
+        else
+          make_p(std::false_type{});
       }
     }
     __syncthreads();
@@ -519,23 +527,31 @@ __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
               dp[nq][ab] = mfma16(va, dof[nq][ks], dp[nq][ab]);
             }
           }
+        // dS = P (dP - D); the masked variant is a separate code path so
+        // that interior tiles carry no per-element compares.
+        auto make_ds = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nq = 0; nq < 2; ++nq) {
-          const int qrow = rw0 + 16 * nq + l16;
-          f32x4 ds[2];
+          for (int nq = 0; nq < 2; ++nq) {
+            const int qrow = rw0 + 16 * nq + l16;
+            f32x4 ds[2];
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab)
+            for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float pv = fast_exp2(fmaf(s[nq][ab][i], c2, -lse2[nq]));
-              if (need_mask) {
-                const int key = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
-                if (key > qrow || key >= k_hi) pv = 0.f;
+              for (int i = 0; i < 4; ++i) {
+                float pv = fast_exp2(fmaf(s[nq][ab][i], c2, -lse2[nq]));
+                if constexpr (decltype(maskc)::value) {
+                  const int key = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
+                  if (key > qrow || key >= k_hi) pv = 0.f;
+                }
+                ds[ab][i] = pv * (dp[nq][ab][i] - drow[nq]);
               }
-              ds[ab][i] = pv * (dp[nq][ab][i] - drow[nq]);
-            }
-          dsb[nq][kp] = pack_bf16x8(ds[0], ds[1]);
-        }
+            dsb[nq][kp] = pack_bf16x8(ds[0], ds[1]);
+          }
+        };
+        if (need_mask)
+          make_ds(std::true_type{});
+        else
+          make_ds(std::false_type{});
       }
       // ---- dQ^T += K^T dS^T
 #pragma unroll
