@@ -126,9 +126,10 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   constexpr int W = kBwdKvWaves;
   constexpr int NG = W / 2;        // key groups of 32 keys
   constexpr int BQ = kBwdKvBM;     // 64 query rows per tile
-  constexpr int BUF = 4 * C::TSZ;  // Q, dO as row tiles, then Q, dO as column tiles
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BQ];  // [buf][lse2 | D][row]
+  constexpr int NS = kBwdKvStages;
+  constexpr int BUF = 2 * C::TSZ;  // Q, dO (column layout, read both ways)
+  __shared__ __attribute__((aligned(16))) __bf16 lds[NS * BUF];
+  __shared__ __attribute__((aligned(16))) float stat[NS][2][BQ];  // [stage][LSE | D][row]
   // P of the current tile, handed from each group's dV wavefront to its dK
   // wavefront: [group][32-row half][16-key block][lane] x 8 fp16 values.
   __shared__ __attribute__((aligned(16))) uint32_t pshare[NG][2][2][64][4];
@@ -188,55 +189,43 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   // Loop-invariant LDS byte offsets of this lane's reads.
   int roff[C::KS], coff[C::NT];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(ks, l16, lg);
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D, kColTile>(ks, l16, lg);
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
 
   const int64_t qstride = (int64_t)hq * D;
-  TileLoader<D, InT, W> lqd;  // Q and dO tiles: same rows and stride
+  using Loader = TileLoader<D, InT, W>;
+  Loader lqd;  // Q and dO tiles: same rows and stride
   lqd.init(wave, lane, qstride);
-  // Staged per-row statistics (base-2 LSE and D) of one query tile; only the
-  // first BQ threads hold one row each.
-  struct RowStat {
-    float lse2, d;
-  };
-  auto stage = [&](const KvStep &s, int buf) __attribute__((always_inline)) -> RowStat {
-    const int32_t *it = items + s.item * kItemWords;
-    const int h = g * G + s.hh;
-    const int nvalid = min(BQ, it[2] - s.qt0);
-    const int64_t row0 = (int64_t)seq_off + s.qt0;
-    __bf16 *b = lds + buf * BUF;
-    const InT *qs = qg + (row0 * hq + h) * D, *ds = dg + (row0 * hq + h) * D;
-    lqd.template issue<kRowTile>(b, qs, nvalid, wave, 0);
-    lqd.template issue<kRowTile>(b + C::TSZ, ds, nvalid, wave, 1);
-    lqd.template issue<kColTile>(b + 2 * C::TSZ, qs, nvalid, wave, 0);
-    lqd.template issue<kColTile>(b + 3 * C::TSZ, ds, nvalid, wave, 1);
-    RowStat st{__builtin_inff(), 0.f};
-    if (tid < nvalid) {
-      const float l = lse[(int64_t)h * T + row0 + tid];
-      // A row without visible keys (LSE = -inf) contributes nothing.
-      st.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-      st.d = delta[(int64_t)h * T + row0 + tid];
-    }
-    return st;
-  };
-  auto commit = [&](int buf, RowStat st) __attribute__((always_inline)) {
-    __bf16 *b = lds + buf * BUF;
-    lqd.template commit<kRowTile>(b, tid, 0);
-    lqd.template commit<kRowTile>(b + C::TSZ, tid, 1);
-    lqd.template commit<kColTile>(b + 2 * C::TSZ, tid, 0);
-    lqd.template commit<kColTile>(b + 3 * C::TSZ, tid, 1);
-    if (tid < BQ) {
-      stat[buf][0][tid] = st.lse2;
-      stat[buf][1][tid] = st.d;
+  // Stage s of the ring: the Q and dO tiles of step `st`, and (wavefront 0)
+  // the tile's natural-log LSE and D rows.
+  auto stage = [&](const KvStep &st, int s) __attribute__((always_inline)) {
+    const int32_t *it = items + st.item * kItemWords;
+    const int h = g * G + st.hh;
+    const int nvalid = min(BQ, it[2] - st.qt0);
+    const int64_t row0 = (int64_t)seq_off + st.qt0;
+    __bf16 *b = lds + s * BUF;
+    lqd.template stage<kColTile>(b, qg + (row0 * hq + h) * D, nvalid);
+    lqd.template stage<kColTile>(b + C::TSZ, dg + (row0 * hq + h) * D, nvalid);
+    if (wave == 0) {
+      stage_row_floats(&stat[s][0][0], lse + (int64_t)h * T + row0, nvalid, lane);
+      stage_row_floats(&stat[s][1][0], delta + (int64_t)h * T + row0, nvalid, lane);
     }
   };
 
   const float c2 = a.scale_log2;
-  KvStep cur = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
-  if (cur.item >= 0) commit(0, stage(cur, 0));
-  wait_staged();
-  __syncthreads();
+  // Two walkers over the same step sequence: `ld` stages NS-1 steps ahead of
+  // `cp`, which is computed.
+  KvStep cp = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
+  KvStep ld = cp;
+  int issued = 0, done = 0;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (ld.item >= 0) {
+      stage(ld, s);
+      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ++issued;
+    }
   // One query tile in two phases separated by a barrier:
   //   A: dV role  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS (fp16);
   //      dK role  dP = dO V^T.
@@ -245,20 +234,23 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   // Rows: half qp, sub-block ab of a 32-row half reads query rows
   // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of a half are the rows
   // 32qp + 8*lg + 0..7 for its key 16nk + l16 -- the A operand layout of the
-  // contraction over query rows.  The LDS buffer index is a compile-time
-  // constant so every LDS read is a precomputed lane offset plus an immediate.
-  auto step = [&](const KvStep cur, auto bufc) __attribute__((always_inline)) -> KvStep {
-    constexpr int buf = decltype(bufc)::value;
-    const KvStep nxt = kv_advance(items, cur, G, seq_off, kt0, kt1);
-    RowStat nst{0.f, 0.f};
-    if (nxt.item >= 0) nst = stage(nxt, buf ^ 1);
-    const int32_t *it = items + cur.item * kItemWords;
+  // contraction over query rows.  The ring slot is a compile-time constant so
+  // every LDS read is a precomputed lane offset plus an immediate.
+  auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
+    constexpr int buf = decltype(slot)::value;
+    wait_stages<2 * Loader::kInstr, NS>(issued - done - 1);
+    __syncthreads();  // stage `buf` visible; the slot staged next is free
+    if (ld.item >= 0) {
+      stage(ld, (buf + NS - 1) % NS);
+      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ++issued;
+    }
+    const int32_t *it = items + cp.item * kItemWords;
     const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
-    const int qt0 = cur.qt0;
+    const int qt0 = cp.qt0;
     const int qt1 = min(qt0 + BQ, q_hi);
     const bool active = has_keys && kw0 < qt1;
-    const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;       // row tiles
-    const __bf16 *Qc = Qs + 2 * C::TSZ, *dOc = Qs + 3 * C::TSZ;  // column tiles
+    const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;
     const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows of the phase-A product
     bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
     f32x4 x[2][2][2];                       // [qp][ab][nk]: S or dP
@@ -281,14 +273,17 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
             for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = mfma16(xa, xf[nk][ks], x[qp][ab][nk]);
           }
       if (!dk_role) {
-        const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi);
+        // Rows past q_hi of a partial tile repeat the last row in LDS and
+        // must drop out here too.
+        const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
         // The masked variant is a separate code path so that interior tiles
         // carry no per-element compares.
         auto make_p = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
           for (int qp = 0; qp < 2; ++qp) {
-            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]);
-            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]);
+            // -LSE in base 2 for rows 32qp + 8lg + 0..7
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]) * -kLog2e;
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]) * -kLog2e;
 #pragma unroll
             for (int nk = 0; nk < 2; ++nk) {
               const int key = kw0 + 16 * nk + l16;
@@ -297,10 +292,10 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
               for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, -(ab ? l1[i] : l0[i])));
+                  float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]));
                   if constexpr (decltype(maskc)::value) {
                     const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
-                    if (key > q || key < k_lo || key >= k_hi) p = 0.f;
+                    if (key > q || key < k_lo || key >= k_hi || q >= q_hi) p = 0.f;
                   }
                   pv[ab][i] = p;
                 }
@@ -340,7 +335,7 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
           }
         }
       }
-      const __bf16 *Bt = dk_role ? Qc : dOc;
+      const __bf16 *Bt = dk_role ? Qs : dOs;
 #pragma unroll
       for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
@@ -350,15 +345,13 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
           for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt, acc[nk][nt]);
         }
     }
-    if (nxt.item >= 0) commit(buf ^ 1, nst);
-    wait_staged();
-    __syncthreads();
-    return nxt;
+    cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
+    ++done;
+    return cp.item >= 0;
   };
-  while (cur.item >= 0) {
-    cur = step(cur, std::integral_constant<int, 0>{});
-    if (cur.item >= 0) cur = step(cur, std::integral_constant<int, 1>{});
-  }
+  if (cp.item >= 0)
+    while (ring_pass<0, NS>(step)) {
+    }
 
   // ---- epilogue: lane holds rows key = kw0 + 16nk + 4lg + i, column 16nt + l16
   GT *outg = static_cast<GT *>(dk_role ? a.dk : a.dv);
@@ -403,8 +396,9 @@ template <int D, typename InT, typename GT>
 __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int BN = kBwdQBN;  // 64 keys per tile
-  constexpr int BUF = 3 * C::TSZ;  // K and V as row tiles, K as a column tile
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
+  constexpr int NS = kBwdQStages;
+  constexpr int BUF = 2 * C::TSZ;  // K (column layout, read both ways), V (row layout)
+  __shared__ __attribute__((aligned(16))) __bf16 lds[NS * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -460,46 +454,52 @@ __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
   auto item_end = [&](int i) __attribute__((always_inline)) { return min(items[i * kItemWords + 4], r1); };
 
   // Loop-invariant LDS byte offsets of this lane's reads.
-  int roff[C::KS], coff[C::NT];
+  int rkoff[C::KS], rvoff[C::KS], coff[C::NT];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(ks, l16, lg);
+  for (int ks = 0; ks < C::KS; ++ks) {
+    rkoff[ks] = row_read_off<D, kColTile>(ks, l16, lg);
+    rvoff[ks] = row_read_off<D, kRowTile>(ks, l16, lg);
+  }
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
 
   const int64_t kstride = (int64_t)hkv * D;
-  TileLoader<D, InT, kBwdQWaves> lkv;  // K and V tiles: same rows and stride
+  using Loader = TileLoader<D, InT, kBwdQWaves>;
+  Loader lkv;  // K and V tiles: same rows and stride
   lkv.init(wave, lane, kstride);
-  auto stage = [&](const QStep &s, int buf) __attribute__((always_inline)) {
-    const int nvalid = min(BN, item_end(s.item) - s.kv0);
-    const int64_t off = (((int64_t)seq_off + s.kv0) * hkv + g) * D;
-    __bf16 *b = lds + buf * BUF;
-    lkv.template issue<kRowTile>(b, kg + off, nvalid, wave, 0);
-    lkv.template issue<kRowTile>(b + C::TSZ, vg + off, nvalid, wave, 1);
-    lkv.template issue<kColTile>(b + 2 * C::TSZ, kg + off, nvalid, wave, 0);
-  };
-  auto commit = [&](int buf) __attribute__((always_inline)) {
-    __bf16 *b = lds + buf * BUF;
-    lkv.template commit<kRowTile>(b, tid, 0);
-    lkv.template commit<kRowTile>(b + C::TSZ, tid, 1);
-    lkv.template commit<kColTile>(b + 2 * C::TSZ, tid, 0);
+  auto stage = [&](const QStep &st, int s) __attribute__((always_inline)) {
+    const int nvalid = min(BN, item_end(st.item) - st.kv0);
+    const int64_t off = (((int64_t)seq_off + st.kv0) * hkv + g) * D;
+    __bf16 *b = lds + s * BUF;
+    lkv.template stage<kColTile>(b, kg + off, nvalid);
+    lkv.template stage<kRowTile>(b + C::TSZ, vg + off, nvalid);
   };
 
   const float c2 = a.scale_log2;
-  QStep cur = q_first_from(items, first + count - 1, first, r1);
-  if (cur.item >= 0) {
-    stage(cur, 0);
-    commit(0);
-  }
-  wait_staged();
-  __syncthreads();
-  auto step = [&](const QStep cur, auto bufc) __attribute__((always_inline)) -> QStep {
-    constexpr int buf = decltype(bufc)::value;
-    const QStep nxt = q_advance(items, cur, first, r1);
-    if (nxt.item >= 0) stage(nxt, buf ^ 1);
-    const int kv0 = cur.kv0;
-    const int k_hi = items[cur.item * kItemWords + 4];
+  // `ld` stages NS-1 steps ahead of `cp`, which is computed.
+  QStep cp = q_first_from(items, first + count - 1, first, r1);
+  QStep ld = cp;
+  int issued = 0, done = 0;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (ld.item >= 0) {
+      stage(ld, s);
+      ld = q_advance(items, ld, first, r1);
+      ++issued;
+    }
+  auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
+    constexpr int buf = decltype(slot)::value;
+    wait_stages<2 * Loader::kInstr, NS>(issued - done - 1);
+    __syncthreads();  // stage `buf` visible; the slot staged next is free
+    if (ld.item >= 0) {
+      stage(ld, (buf + NS - 1) % NS);
+      ld = q_advance(items, ld, first, r1);
+      ++issued;
+    }
+    const int kv0 = cp.kv0;
+    const int k_hi = items[cp.item * kItemWords + 4];
     if (has_rows && kv0 <= rw_end - 1) {
-      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ, *Kc = Ks + 2 * C::TSZ;
+      const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ;
       const bool need_mask = (kv0 + BN - 1 > rw0) || (kv0 + BN > k_hi);
       bf16x8 dsb[2][2];
       // Each 32-key pair kp is finished (scores -> dS) before the next one
@@ -519,8 +519,8 @@ __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
-            const bf16x8 ka = lds_row8(Ks, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
-            const bf16x8 va = lds_row8(Vs, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
+            const bf16x8 ka = lds_row8(Ks, rkoff[ks] + (32 * kp + 4 * ab) * 2 * D);
+            const bf16x8 va = lds_row8(Vs, rvoff[ks] + (32 * kp + 4 * ab) * 2 * D);
 #pragma unroll
             for (int nq = 0; nq < 2; ++nq) {
               s[nq][ab] = mfma16(ka, qf[nq][ks], s[nq][ab]);
@@ -558,20 +558,18 @@ __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
       for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          const bf16x8 ka = lds_col8<D>(Kc, coff[nt] + 32 * kp * 2 * D);
+          const bf16x8 ka = lds_col8<D>(Ks, coff[nt] + 32 * kp * 2 * D);
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka, dsb[nq][kp], dq[nq][nt]);
         }
     }
-    if (nxt.item >= 0) commit(buf ^ 1);
-    wait_staged();
-    __syncthreads();
-    return nxt;
+    cp = q_advance(items, cp, first, r1);
+    ++done;
+    return cp.item >= 0;
   };
-  while (cur.item >= 0) {
-    cur = step(cur, std::integral_constant<int, 0>{});
-    if (cur.item >= 0) cur = step(cur, std::integral_constant<int, 1>{});
-  }
+  if (cp.item >= 0)
+    while (ring_pass<0, NS>(step)) {
+    }
 
   // ---- epilogue: lane holds dQ[row = rw0 + 16nq + l16][16nt + 4lg + i]
   GT *dqg = static_cast<GT *>(a.dq);

@@ -37,6 +37,7 @@ struct FwdCfg {
   static constexpr int KP = BN / 32;       // 32-key pairs per tile
   static constexpr int TSZ = BN * D;       // one swizzled tile (bf16 elements)
   static constexpr int BUF = 2 * TSZ;      // K (row tile), V (column tile)
+  static constexpr int NS = kFwdStages;    // LDS ring depth
 };
 static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * 32, "forward tile shape");
 
@@ -82,7 +83,8 @@ __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x4 &v) {
 template <int D, typename InT, typename OutT>
 __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::BUF];
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[NS * C::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,30 +148,38 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
     for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // K and V tiles of 64 keys starting at key kvs, staged into LDS buffer buf.
+  // K and V tiles of 64 keys starting at key kvs, staged into ring slot `slot`.
   const int64_t kvstride = (int64_t)hkv * D;
-  TileLoader<D, InT, C::W> lkv;
+  using Loader = TileLoader<D, InT, C::W>;
+  Loader lkv;
   lkv.init(wave, lane, kvstride);
-  auto stage = [&](int kvs, int buf) __attribute__((always_inline)) {
-    __bf16 *Ks = lds + buf * C::BUF;
+  auto stage = [&](int kvs, int slot) __attribute__((always_inline)) {
+    __bf16 *Ks = lds + slot * C::BUF;
     const int64_t off = ((int64_t)(seq_off + kvs) * hkv + g) * D;
-    lkv.template issue<kRowTile>(Ks, kg + off, ke - kvs, wave, 0);
-    lkv.template issue<kColTile>(Ks + C::TSZ, vg + off, ke - kvs, wave, 1);
-  };
-  auto commit = [&](int buf) __attribute__((always_inline)) {
-    __bf16 *Ks = lds + buf * C::BUF;
-    lkv.template commit<kRowTile>(Ks, tid, 0);
-    lkv.template commit<kColTile>(Ks + C::TSZ, tid, 1);
+    lkv.template stage<kRowTile>(Ks, kg + off, ke - kvs);
+    lkv.template stage<kColTile>(Ks + C::TSZ, vg + off, ke - kvs);
   };
 
   const float c2 = a.scale_log2;
+  int issued = 0, j = 0;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (issued < ntiles) {
+      stage(kb + issued * C::BN, s);
+      ++issued;
+    }
 
-  // One key tile: the LDS buffer index is a compile-time constant so every
-  // LDS read is a precomputed lane offset plus an immediate.
-  auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
+  // One key tile.  The ring slot is a compile-time constant so every LDS
+  // read is a precomputed lane offset plus an immediate.
+  auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
+    constexpr int buf = decltype(slot)::value;
+    wait_stages<2 * Loader::kInstr, NS>(issued - j - 1);
+    __syncthreads();  // tile `buf` visible; the slot staged next is free
+    if (issued < ntiles) {
+      stage(kb + issued * C::BN, (buf + NS - 1) % NS);
+      ++issued;
+    }
     const int kv0 = kb + j * C::BN;
-    if (j + 1 < ntiles) stage(kv0 + C::BN, buf ^ 1);
     const __bf16 *Ks = lds + buf * C::BUF;
     const __bf16 *Vs = Ks + C::TSZ;
 
@@ -197,27 +207,36 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
           }
       }
 
-      // ---- online softmax (base 2), one query row per lane and subtile.
+      // ---- masking (boundary tiles only: a separate code path, so that
+      // interior tiles carry no per-element compares)
       const bool need_mask = (kv0 + C::BN - 1 > rw0) || (kv0 + C::BN > k_hi);
+      if (need_mask) {
+#pragma unroll
+        for (int nq = 0; nq < C::NQ; ++nq) {
+          const int qrow = rw0 + 16 * nq + l16;
+#pragma unroll
+          for (int kp = 0; kp < C::KP; ++kp)
+#pragma unroll
+            for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kv = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
+                if (kv > qrow || kv >= k_hi) s[nq][kp][ab][i] = kNegInf;
+              }
+        }
+      }
+
+      // ---- online softmax (base 2), one query row per lane and subtile.
       bf16x8 pf[C::NQ][C::KP];
 #pragma unroll
       for (int nq = 0; nq < C::NQ; ++nq) {
-        const int qrow = rw0 + 16 * nq + l16;
         float mx = kNegInf;
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float val = s[nq][kp][ab][i];
-              if (need_mask) {
-                const int kv = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
-                if (kv > qrow || kv >= k_hi) val = kNegInf;
-                s[nq][kp][ab][i] = val;
-              }
-              mx = fmaxf(mx, val);
-            }
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[nq][kp][ab][i]);
         mx = wave_max_xor16_32(mx, xl) * c2;
         // Lazy rescale: the running maximum m_run only moves when a row's
         // maximum exceeds it by more than 8 (so every p <= 2^8); softmax is
@@ -258,22 +277,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
           for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf, pf[nq][kp], o[nq][mt]);
         }
     }
-
-    if (j + 1 < ntiles) commit(buf ^ 1);
-    wait_staged();
-    __syncthreads();
+    ++j;
+    return j < ntiles;
   };
-
-  if (ntiles > 0) {
-    stage(kb, 0);
-    commit(0);
-  }
-  wait_staged();
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
-  }
+  if (ntiles > 0)
+    while (ring_pass<0, NS>(step)) {
+    }
 
   // ---- epilogue: normalise, optional merge, write O rows and LSE.
   OutT *__restrict__ og = static_cast<OutT *>(a.o);

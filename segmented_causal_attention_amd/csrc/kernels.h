@@ -16,15 +16,16 @@ namespace segattn {
 constexpr int kItemWords = 8;
 
 // Forward tile shape: kFwdWaves wavefronts x 32 query rows per workgroup,
-// 64 keys per K/V tile staged through LDS.
-constexpr int kFwdWaves = 4;
+// 64 keys per K/V tile staged through LDS in a ring of kFwdStages tiles.
+constexpr int kFwdWaves = 8;
 constexpr int kFwdBM = 32 * kFwdWaves;
 constexpr int kFwdBN = 64;
+constexpr int kFwdStages = 4;
 
 // Backward tile shapes.
 //   dK/dV kernel: 128 keys per workgroup (4 key groups x 32 keys, each with
 //                 a dV wavefront and a dK wavefront), 64 query rows per
-//                 staged Q/dO tile.
+//                 staged Q/dO tile pair.
 //   dQ kernel:    256 query rows per workgroup (8 waves x 32 rows), 64 keys
 //                 per staged K/V tile.
 constexpr int kBwdKvWaves = 8;
@@ -33,6 +34,9 @@ constexpr int kBwdKvBM = 64;
 constexpr int kBwdQWaves = 8;
 constexpr int kBwdQBM = 32 * kBwdQWaves;
 constexpr int kBwdQBN = 64;
+// Depth of the LDS prefetch rings (tiles in flight + the one in use).
+constexpr int kBwdKvStages = 4;
+constexpr int kBwdQStages = 4;
 
 struct FwdArgs {
   const void *q, *k, *v;

@@ -11,16 +11,21 @@
 //     over rows; each half-wavefront visits rows 8g + b of g in {0,1} (or
 //     {2,3}), two chunks each, and needs eight disjoint 32-byte bank windows.
 //     swz = ((r >> 3) & 1) << 3 | (r & 3) << 1 | (r >> 4) & 1.
-// Both were measured bank-conflict free on the device (SQ_LDS_BANK_CONFLICT);
-// each is 2-way conflicted under the other access, so a tensor read both ways
-// is staged twice.  For D = 64 (8 chunks per row) the swizzle is taken mod 8.
-// Without padding a wavefront fills 1 KB of a tile with one
-// global_load_lds_dwordx4 (global memory straight to LDS, no registers).
+// Both were measured bank-conflict free on the device (SQ_LDS_BANK_CONFLICT).
+// A tensor that is read both ways (Q and dO in the dK/dV kernel, K in the dQ
+// kernel) is staged once, in the column layout: its row reads then run at
+// about 60% of the row layout's LDS rate (measured), which costs far less
+// than copying the tile from memory twice.  For D = 64 (8 chunks per row) the
+// swizzle is taken mod 8.  Without padding a wavefront fills 1 KB of a tile
+// with one global_load_lds_dwordx4 (global memory straight to LDS, no
+// registers).
 //
 // The per-lane byte offsets of every read are loop invariant; kernels compute
 // them once (row_read_off / col_read_off) and add compile-time immediates for
 // the pair, half and buffer indices (the swizzles ignore row bits 2 and 5).
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -47,17 +52,17 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
 
 // Row reads.  Lane (l16, lg) of step ks reads 8 consecutive columns of row
 // rho(l16) = 8*(l16/4) + l16%4 (plus a multiple of 4 rows added as an
-// immediate, which leaves f unchanged) at logical chunk 4*ks + lg.
-// Returns the byte offset for step ks.
-template <int D>
+// immediate, which leaves both swizzles unchanged) at logical chunk 4*ks + lg.
+// Returns the byte offset for step ks in a tile of the given kind.
+template <int D, int KIND = kRowTile>
 __device__ __forceinline__ int row_read_off(int ks, int l16, int lg) {
   const int r = 8 * (l16 >> 2) + (l16 & 3);
-  return chunk_off<D, kRowTile>(r, 4 * ks + lg);
+  return chunk_off<D, KIND>(r, 4 * ks + lg);
 }
 
-// Transposing reads.  For column block mt (16 columns) lane (l16, lg) points
-// at row 8*lg + l16/4 (plus multiples of 4 rows as immediates), columns
-// 16*mt + 4*(l16%4) .. +3.  Returns the byte offset.
+// Transposing reads (column tiles).  For column block mt (16 columns) lane
+// (l16, lg) points at row 8*lg + l16/4 (plus multiples of 4 rows as
+// immediates), columns 16*mt + 4*(l16%4) .. +3.  Returns the byte offset.
 template <int D>
 __device__ __forceinline__ int col_read_off(int mt, int l16, int lg) {
   const int r = 8 * lg + (l16 >> 2);
@@ -90,12 +95,12 @@ __device__ __forceinline__ bf16x8 lds_col8(const void *base, int byte_off) {
 // Rows >= nvalid are filled from row nvalid-1 (bf16 path) or with zeros
 // (fp32 path); the kernels mask them, they only need to be finite.
 //   init(): stride = elements between consecutive rows of the tensor;
-//   issue<KIND>(): src = first row of the tile; KIND = tile layout.
-// bf16: issue() starts direct global->LDS copies; the caller waits for them
-//   (wait_staged) before the barrier that publishes the tile.  commit() does
-//   nothing.
-// fp32: issue() loads into a register slot, commit() rounds to bf16 and
-//   stores (used only for fp32 inputs; one loader stages two tensors).
+//   stage<KIND>(): src = first row of the tile; KIND = tile layout.
+// bf16: stage() starts kInstr direct global->LDS copies per wavefront and
+//   returns; wait_vm / wait_stages below wait for them before the barrier
+//   that publishes the tile.
+// fp32: stage() loads, rounds to bf16 and stores with ordinary LDS writes
+//   (only used for fp32 inputs; the barrier publishes them).
 template <int D, typename InT, int W>
 struct TileLoader;
 
@@ -104,10 +109,11 @@ struct TileLoader<D, __bf16, W> {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;           // rows per wavefront instruction
   static constexpr int NI = kTileRows / RPI / W;  // instructions per wavefront
+  static constexpr int kInstr = NI;
   static_assert(NI >= 1 && NI * RPI * W == kTileRows, "tile split");
   int row_[NI];     // lane's tile row per instruction
   int off_[2][NI];  // element offset of the lane's chunk in a full tile, per tile kind
-  int stride_;      // elements between rows (< 2^31 / 64 is checked on the host)
+  int stride_;      // elements between rows (64 * stride < 2^31: heads <= 65536, d <= 128)
   int wave_;        // wavefront index (scalar)
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
     stride_ = (int)stride;
@@ -120,7 +126,7 @@ struct TileLoader<D, __bf16, W> {
     }
   }
   template <int KIND>
-  __device__ __forceinline__ void issue(__bf16 *tile, const __bf16 *src, int nvalid, int, int = 0) const {
+  __device__ __forceinline__ void stage(__bf16 *tile, const __bf16 *src, int nvalid) const {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       int off = off_[KIND][t];
@@ -131,42 +137,83 @@ struct TileLoader<D, __bf16, W> {
                                        16, 0, 0);
     }
   }
-  template <int KIND>
-  __device__ __forceinline__ void commit(__bf16 *, int, int = 0) const {}
 };
 
 template <int D, int W>
 struct TileLoader<D, float, W> {
   static constexpr int CPR = D / 8;
   static constexpr int N = (kTileRows * CPR + 64 * W - 1) / (64 * W);  // chunks per thread
-  u32x4 r_[2][N];  // two staged tensors (slot 0 / 1)
+  static constexpr int kInstr = 0;  // nothing left in flight after stage()
   int64_t stride_;
-  __device__ __forceinline__ void init(int, int, int64_t stride) { stride_ = stride; }
-  // fp32 path: issue<KIND>(...) loads into register slot `slot` (the tile
-  // pointer is unused until commit).
-  template <int KIND>
-  __device__ __forceinline__ void issue(__bf16 *, const float *src, int nvalid, int wave, int slot = 0) {
-    const int tid = wave * 64 + (int)(threadIdx.x & 63);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int ch = tid + 64 * W * i, row = ch / CPR, c = ch % CPR;
-      r_[slot][i] = (row < kTileRows && row < nvalid) ? load8<float>(src + row * stride_ + 8 * c) : (u32x4){0, 0, 0, 0};
-    }
+  int tid_;
+  __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
+    stride_ = stride;
+    tid_ = wave * 64 + lane;
   }
   template <int KIND>
-  __device__ __forceinline__ void commit(__bf16 *tile, int tid, int slot = 0) const {
+  __device__ __forceinline__ void stage(__bf16 *tile, const float *src, int nvalid) const {
+    u32x4 r[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int ch = tid + 64 * W * i, row = ch / CPR, c = ch % CPR;
+      const int ch = tid_ + 64 * W * i, row = ch / CPR, c = ch % CPR;
+      r[i] = (row < kTileRows && row < nvalid) ? load8<float>(src + row * stride_ + 8 * c) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ch = tid_ + 64 * W * i, row = ch / CPR, c = ch % CPR;
       if (row < kTileRows)
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(tile) + chunk_off<D, KIND>(row, c)) = r_[slot][i];
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(tile) + chunk_off<D, KIND>(row, c)) = r[i];
     }
   }
 };
 
-// Waits for this wavefront's outstanding memory operations (including the
-// direct global->LDS copies) before a barrier publishes a staged tile.
-__device__ __forceinline__ void wait_staged() { __builtin_amdgcn_s_waitcnt(0); }
+// 64 consecutive floats (one per lane; lanes >= nvalid repeat element
+// nvalid-1) copied straight into LDS by one wavefront.
+__device__ __forceinline__ void stage_row_floats(float *dst, const float *src, int nvalid, int lane) {
+  __builtin_amdgcn_global_load_lds((const void *)(src + min(lane, nvalid - 1)),
+                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+}
+
+// Waits until at most N of this wavefront's vector memory operations are
+// still outstanding (loads complete in issue order).  Only the vmcnt field is
+// constrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Prefetch ring: before computing on stage j, wait for this wavefront's
+// copies of stage j while `ahead` (0 .. NS-2, wave-uniform) later stages,
+// L copies each, may stay in flight.  L = 0 (register staging) waits for all.
+template <int L, int NS>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (L > 0 && NS >= 4) {
+    if (ahead >= 2) {
+      wait_vm<2 * L>();
+      return;
+    }
+  }
+  if constexpr (L > 0 && NS >= 3) {
+    if (ahead >= 1) {
+      wait_vm<L>();
+      return;
+    }
+  }
+  wait_vm<0>();
+}
+
+// Runs f(integral_constant<B>) for B = 0 .. NS-1 while it returns true; the
+// ring slot of every step is a compile-time constant.
+template <int B, int NS, typename F>
+__device__ __forceinline__ bool ring_pass(F &f) {
+  if constexpr (B == NS) {
+    return true;
+  } else {
+    if (!f(std::integral_constant<int, B>{})) return false;
+    return ring_pass<B + 1, NS>(f);
+  }
+}
 
 }  // namespace dev
 }  // namespace segattn
