@@ -38,4 +38,6 @@ from .attention import (  # noqa: F401
     attention_bwd,
     segmented_bwd,
     attention_rows,
+    attention_rows_bwd,
+    attention_keys_bwd,
 )

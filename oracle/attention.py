@@ -270,3 +270,57 @@ def attention_rows(q_rows, k_seq, v_seq, row_pos, scale, key_block=65536):
         p, l_ = _softmax_rows(z)
         o, lse = merge(o, lse, (p @ V)[:, None, :], l_[None, :])
     return o[:, 0, :], lse[0]
+
+
+def attention_rows_bwd(q_rows, do_rows, k_seq, v_seq, row_pos, scale, key_block=65536):
+    """dQ of selected query rows of ONE head of one sequence (rows as in
+    ``attention_rows``), for the upstream gradient dO of those rows.
+
+    The definition restricted to row i: D_i = <dO_i, O_i> with the row's own
+    O_i (from ``attention_rows``), then over the visible keys j <= i
+      P_ij = exp(z_ij - LSE_i),  dP_ij = <dO_i, V_j>,
+      dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale * sum_j dS_ij K_j,
+    accumulated over key blocks.  Returns dQ [n, d]."""
+    o, lse = attention_rows(q_rows, k_seq, v_seq, row_pos, scale, key_block)
+    Q, dO = _f64(q_rows), _f64(do_rows)
+    pos = np.asarray(row_pos, dtype=np.int64)
+    D = np.sum(dO * o, axis=1)
+    dq = np.zeros_like(Q)
+    kmax = int(pos.max()) + 1 if len(pos) else 0
+    for k0 in range(0, kmax, key_block):
+        k1 = min(k0 + key_block, kmax)
+        K = _f64(k_seq[k0:k1])
+        V = _f64(v_seq[k0:k1])
+        vis = np.arange(k0, k1)[None, :] <= pos[:, None]
+        with np.errstate(invalid="ignore"):
+            P = np.where(vis, np.exp(scale * (Q @ K.T) - lse[:, None]), 0.0)
+        dS = P * (dO @ V.T - D[:, None])
+        dq += scale * (dS @ K)
+    return dq
+
+
+def attention_keys_bwd(q_seq, k_seq, v_seq, do_seq, key_pos, scale):
+    """dK and dV of selected keys of ONE head of one sequence: key j
+    receives from every row i >= j of the sequence.
+
+    The definition restricted to key j: with O_i, LSE_i of the rows
+    i >= min(key_pos) (from ``attention_rows``) and D_i = <dO_i, O_i>,
+      dV_j = sum_{i >= j} P_ij dO_i,
+      dK_j = scale * sum_{i >= j} P_ij (<dO_i, V_j> - D_i) Q_i.
+    q_seq, do_seq [L, d] (one query head); k_seq, v_seq [L, d].  For grouped
+    heads the caller sums over the query heads of the group.
+    Returns (dK [n, d], dV [n, d])."""
+    kp = np.asarray(key_pos, dtype=np.int64)
+    L = len(q_seq)
+    rows = np.arange(int(kp.min()), L)
+    o, lse = attention_rows(q_seq[rows], k_seq, v_seq, rows, scale)
+    Q, dO = _f64(q_seq[rows]), _f64(do_seq[rows])
+    D = np.sum(dO * o, axis=1)
+    Kj, Vj = _f64(k_seq[kp]), _f64(v_seq[kp])
+    vis = rows[:, None] >= kp[None, :]
+    with np.errstate(invalid="ignore"):
+        P = np.where(vis, np.exp(scale * (Q @ Kj.T) - lse[:, None]), 0.0)
+    dv = P.T @ dO
+    dS = P * (dO @ Vj.T - D[:, None])
+    dk = scale * (dS.T @ Q)
+    return dk, dv

@@ -223,6 +223,39 @@ def test_attention_rows_matches_full():
     np.testing.assert_allclose(lrow, lse[0, rows], rtol=1e-13, atol=1e-13)
 
 
+
+def test_attention_rows_bwd_matches_full_gradient():
+    """dQ of sampled rows, key-blocked, equals the full-gradient oracle's rows
+    (which finite differences and autograd pin below)."""
+    S, d, scale = 700, 16, 0.25
+    q, k, v, do = rand((S, 1, d), 60), rand((S, 1, d), 61), rand((S, 1, d), 62), rand((S, 1, d), 63)
+    dq, _, _ = A.attention_bwd(q, k, v, do, None, scale)
+    rows = np.array([0, 1, 99, 255, 256, 511, 699])
+    got = A.attention_rows_bwd(q[rows, 0], do[rows, 0], k[:, 0], v[:, 0], rows, scale, key_block=128)
+    np.testing.assert_allclose(got, dq[rows, 0], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 2)])
+def test_attention_keys_bwd_matches_full_gradient(hq, hkv):
+    """dK/dV of sampled keys (summed over the query heads of each KV head)
+    equal the full-gradient oracle's rows."""
+    S, d, scale = 300, 8, 0.4
+    q, k, v, do = rand((S, hq, d), 64), rand((S, hkv, d), 65), rand((S, hkv, d), 66), rand((S, hq, d), 67)
+    _, dk, dv = A.attention_bwd(q, k, v, do, None, scale)
+    keys = np.array([0, 7, 150, 298, 299])
+    for g in range(hkv):
+        gk = np.zeros((len(keys), d))
+        gv = np.zeros((len(keys), d))
+        for h in range(hq):
+            if A.kv_head_of(h, hq, hkv) != g:
+                continue
+            a, b = A.attention_keys_bwd(q[:, h], k[:, g], v[:, g], do[:, h], keys, scale)
+            gk += a
+            gv += b
+        np.testing.assert_allclose(gk, dk[keys, g], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(gv, dv[keys, g], rtol=1e-11, atol=1e-12)
+
+
 # ----------------------------------------------------------------- backward
 
 def _f(q, k, v, do, cu, scale):
