@@ -15,7 +15,7 @@
 //   4 groups of 32; each group is handled by two wavefronts on one SIMD.  It
 //   walks every (item, query head of the group, 64-row query tile) that can
 //   see its keys.  Per tile, the dV wavefront computes S = Q K^T and P and
-//   hands P (fp16) to the dK wavefront through LDS while that one computes
+//   hands P (bf16) to the dK wavefront through LDS while that one computes
 //   dP = dO V^T; after a barrier the first accumulates dV += P^T dO, the
 //   second dS = P (dP - D) and dK += dS^T Q.  Each wavefront keeps only its
 //   own key-side operand (K or V) and accumulator in registers, so two fit
@@ -131,7 +131,9 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[NS * BUF];
   __shared__ __attribute__((aligned(16))) float stat[NS][2][BQ];  // [stage][LSE | D][row]
   // P of the current tile, handed from each group's dV wavefront to its dK
-  // wavefront: [group][32-row half][16-key block][lane] x 8 fp16 values.
+  // wavefront: [group][32-row half][16-key block][lane] x 8 bf16 values (the
+  // very operand of dV += P^T dO; bf16 keeps fp32's exponent range, which
+  // matters at a million keys where P ~ 1e-6 would be subnormal in fp16).
   __shared__ __attribute__((aligned(16))) uint32_t pshare[NG][2][2][64][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
       ++issued;
     }
   // One query tile in two phases separated by a barrier:
-  //   A: dV role  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS (fp16);
+  //   A: dV role  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS (bf16);
   //      dK role  dP = dO V^T.
   //   B: dV role  dV += P^T dO;
   //      dK role  dS = P (dP - D) with P from LDS, dK += dS^T Q.
@@ -300,9 +302,7 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
                   pv[ab][i] = p;
                 }
               opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
-              const u32x4 ph = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
-                                pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
-              *reinterpret_cast<u32x4 *>(pshare[kgrp][qp][nk][lane]) = ph;
+              *reinterpret_cast<bf16x8 *>(pshare[kgrp][qp][nk][lane]) = opa[qp][nk];
             }
           }
         };
@@ -328,7 +328,8 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
             for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float p = f16_at(ph[2 * ab + (i >> 1)], i & 1);
+                const uint32_t w = ph[2 * ab + (i >> 1)];
+                const float p = (i & 1) ? bf16_hi(w) : bf16_lo(w);
                 ds[ab][i] = p * (x[qp][ab][nk][i] - (ab ? d1[i] : d0[i]));
               }
             opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);

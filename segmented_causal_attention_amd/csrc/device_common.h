@@ -40,15 +40,6 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4 &a, const f32x4 &b) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Two floats -> two fp16 (round toward zero) packed in one dword, and back.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-__device__ __forceinline__ float f16_at(uint32_t w, int hi) {
-  return (float)__builtin_bit_cast(f16x2, w)[hi];
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
