@@ -1,6 +1,7 @@
 """Benchmark of the segmented causal attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu-baseline]
+                    [--no-hbm-kernels]
 
 One step = one pass of the whole path over one synthetic batch, inputs resident
 in HBM: the host planner cuts the sequence into FLOPs-balanced segments, the
@@ -41,6 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-hbm-kernels", action="store_true",
+                   help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
                    help="token prefix of one head timed for the CPU oracle baseline")
     return p.parse_args()
@@ -177,6 +180,52 @@ def cpu_baseline(W, synth, tokens, heads=2):
                       f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s; cpu: {model}"}
 
 
+def hbm_kernels(torch, sa, W):
+    """HBM-bound kernels of the path, each timed alone with HIP events on the
+    launch stream (mean of 10 launches after 2 warm-up launches):
+      merge  -- segattn_merge of two fp32 partials shaped like one ring
+                segment pass at 131072 tokens x 32 heads x 128 dims, out of
+                place: (3 * 4 * d + 12) bytes per (row, head);
+      D      -- the backward reduction D = <dO, O> of this workload
+                (segattn_bwd_preprocess): (2 * 2 * d + 4) bytes per (row, head)
+                for bf16 O and dO."""
+    E = torch.cuda.Event
+
+    def timed(fn, n=10):
+        for _ in range(2):
+            fn()
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {}
+    rows, h, d = 131072, 32, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    oa = torch.randn((rows, h, d), generator=g, device="cuda")
+    ob = torch.randn((rows, h, d), generator=g, device="cuda")
+    la = torch.randn((h, rows), generator=g, device="cuda")
+    lb = torch.randn((h, rows), generator=g, device="cuda")
+    oo, lo = torch.empty_like(oa), torch.empty_like(la)
+    ms = timed(lambda: sa.segattn_merge(oa, la, ob, lb, o_out=oo, lse_out=lo))
+    nbytes = (3 * 4 * d + 12) * rows * h
+    out["merge"] = {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "ms": round(ms, 4), "bytes": nbytes, "shape": [rows, h, d]}
+    del oa, ob, la, lb, oo, lo
+    rev = W.items[::-1].copy()
+    ms = timed(lambda: sa.segattn_bwd_preprocess(W.q, W.k, W.o, W.do, rev, W.bws))
+    nbytes = ((W.o.element_size() + W.do.element_size()) * W.d + 4) * W.T * W.hq
+    out["bwd_preprocess"] = {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "ms": round(ms, 4), "bytes": nbytes}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -213,12 +262,14 @@ def main():
 
     flops = W.flops_fwd + W.flops_bwd
     value = flops / (ms / 1e3) / 1e12
-    # Dominant launch: the backward main call (key-stationary dK/dV and
-    # query-stationary dQ kernels) or the forward call, whichever is longer.
+    # Dominant kernel: bwd_kernel (one launch per segattn_bwd call, after two
+    # tiny table uploads) or fwd_kernel (one launch per segattn_fwd call),
+    # whichever takes longer per step; ring workloads launch the forward once
+    # per ring step, and the reported time is their sum.
     if bwd_ms >= fwd_ms:
-        dom, dom_ms, dom_flops = "segattn_bwd (dkdv_kernel + dq_kernel)", bwd_ms, W.flops_bwd
+        dom, dom_ms, dom_flops = "bwd_kernel (segattn_bwd)", bwd_ms, W.flops_bwd
     else:
-        dom, dom_ms, dom_flops = "segattn_fwd (fwd_kernel)", fwd_ms, W.flops_fwd
+        dom, dom_ms, dom_flops = "fwd_kernel (segattn_fwd)", fwd_ms, W.flops_fwd
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     out = {
         "metric": "segmented causal attn fwd+bwd TFLOP/s and % of bf16 MFMA peak, 1 GPU",
@@ -241,6 +292,8 @@ def main():
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
+    if not args.no_hbm_kernels:
+        out["hbm_kernels"] = hbm_kernels(torch, sa, W)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, synth, args.cpu_tokens)
     print(json.dumps(out), flush=True)

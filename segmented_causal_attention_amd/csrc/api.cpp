@@ -367,8 +367,9 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   if (!workspace || ws_bytes < need)
     return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
-  if ((int64_t)plan.n_kv_units * shape->hkv > 0x7fffffffLL || (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL)
-    return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
+  const int64_t kv_blocks = (int64_t)plan.n_kv_units * shape->hkv;
+  const int64_t kv_pad = (kv_blocks + 7) / 8 * 8;
+  if (kv_pad + (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
@@ -384,9 +385,14 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
     PreArgs pa{o, d_o, delta, shape->tokens, shape->hq};
     if (hipError_t e = launch_bwd_pre(pa, shape->d, o_dtype, shape->in_dtype, s)) return device_error(e, fn);
   }
-  if (hipError_t e = launch_upload(d_items, plan.items.data(), (int64_t)plan.items.size(), s)) return device_error(e, fn);
-  if (hipError_t e = launch_upload(d_kvg, plan.kvg.data(), (int64_t)plan.kvg.size(), s)) return device_error(e, fn);
-  if (hipError_t e = launch_upload(d_qg, plan.qg.data(), (int64_t)plan.qg.size(), s)) return device_error(e, fn);
+  {
+    // the three tables are contiguous in the workspace: one upload
+    std::vector<int32_t> words((size_t)((char *)d_qg - (char *)d_items) / 4 + plan.qg.size(), 0);
+    std::copy(plan.items.begin(), plan.items.end(), words.begin());
+    std::copy(plan.kvg.begin(), plan.kvg.end(), words.begin() + (d_kvg - d_items));
+    std::copy(plan.qg.begin(), plan.qg.end(), words.begin() + (d_qg - d_items));
+    if (hipError_t e = launch_upload(d_items, words.data(), (int64_t)words.size(), s)) return device_error(e, fn);
+  }
 
   BwdArgs a;
   a.q = q;
@@ -406,13 +412,14 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   a.n_qg = (int32_t)(plan.qg.size() / 4);
   a.n_kv_units = plan.n_kv_units;
   a.n_q_units = plan.n_q_units;
+  a.kv_blocks = (int32_t)kv_blocks;
+  a.kv_pad = (int32_t)kv_pad;
   a.tokens = shape->tokens;
   a.hq = shape->hq;
   a.hkv = shape->hkv;
   a.scale = shape->scale;
   a.scale_log2 = shape->scale * 1.4426950408889634f;
   a.accumulate = (flags & SEGATTN_ACCUMULATE) ? 1 : 0;
-  if (hipError_t e = launch_bwd_dkdv(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
-  if (hipError_t e = launch_bwd_dq(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
+  if (hipError_t e = launch_bwd(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
   return SEGATTN_OK;
 }

@@ -11,7 +11,8 @@
 // over the items in REVERSE item order, so no atomics are needed and the
 // result is deterministic.
 //
-// dkdv_kernel: key-stationary.  A workgroup owns 128 keys of one KV head in
+// One kernel, two kinds of workgroup (bwd_kernel at the end of this file):
+// dK/dV role: key-stationary.  A workgroup owns 128 keys of one KV head in
 //   4 groups of 32; each group is handled by two wavefronts on one SIMD.  It
 //   walks every (item, query head of the group, 64-row query tile) that can
 //   see its keys.  Per tile, the dV wavefront computes S = Q K^T and P and
@@ -22,7 +23,7 @@
 //   on every SIMD, and the two do equal MFMA work (4 products per tile).  Q
 //   and dO tiles are staged row-major; the operands contracted over query
 //   rows are read with transposing LDS reads.
-// dq_kernel: query-stationary, like the forward.  A workgroup owns 256 query
+// dQ role: query-stationary, like the forward.  A workgroup owns 256 query
 //   rows of one head (8 waves x 32 rows, two per SIMD; Q and dO in registers)
 //   and walks the
 //   64-key tiles of every item of its query group; per tile it recomputes
@@ -120,21 +121,33 @@ __device__ __forceinline__ KvStep kv_advance(const int32_t *items, KvStep s, int
   return kv_first_from(items, s.item - 1, seq_off, kt0, kt1);
 }
 
+// LDS of the backward kernel, shared by its two roles: the 64-row tile ring
+// (both roles), and for the dK/dV role the staged row statistics and the
+// P hand-over buffer.
+template <int D>
+struct BwdSmem {
+  static constexpr int kRing = kBwdKvStages * 2 * kTileRows * D;  // bf16 elements
+  __bf16 *ring;
+  float (*stat)[2][kBwdKvBM];                      // [stage][LSE | D][row]
+  uint32_t (*pshare)[2][2][64][4];                 // [group][half][key block][lane] x 4 dwords
+};
+
 template <int D, typename InT, typename GT>
-__global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem<D> &sm) {
   using C = BwdCfg<D>;
   constexpr int W = kBwdKvWaves;
   constexpr int NG = W / 2;        // key groups of 32 keys
   constexpr int BQ = kBwdKvBM;     // 64 query rows per tile
   constexpr int NS = kBwdKvStages;
   constexpr int BUF = 2 * C::TSZ;  // Q, dO (column layout, read both ways)
-  __shared__ __attribute__((aligned(16))) __bf16 lds[NS * BUF];
-  __shared__ __attribute__((aligned(16))) float stat[NS][2][BQ];  // [stage][LSE | D][row]
+  static_assert(NS * BUF == BwdSmem<D>::kRing && NG == 4, "backward LDS layout");
+  __bf16 *lds = sm.ring;
+  float(*stat)[2][BQ] = sm.stat;
   // P of the current tile, handed from each group's dV wavefront to its dK
   // wavefront: [group][32-row half][16-key block][lane] x 8 bf16 values (the
   // very operand of dV += P^T dO; bf16 keeps fp32's exponent range, which
   // matters at a million keys where P ~ 1e-6 would be subnormal in fp16).
-  __shared__ __attribute__((aligned(16))) uint32_t pshare[NG][2][2][64][4];
+  uint32_t(*pshare)[2][2][64][4] = sm.pshare;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(64 * kBwdKvWaves) void dkdv_kernel(BwdArgs a) {
   const bool dk_role = wave >= NG;
 
   int rank, g;
-  map_head(blockIdx.x, a.hkv, rank, g);
+  map_head(x, a.hkv, rank, g);
   const int32_t *kv = a.kvg + find_unit(a.kvg, 4, 3, a.n_kvg, rank) * 4;
   const int seq_off = kv[0], kb = kv[1], ke = kv[2];
   const int kt0 = kb + (rank - kv[3]) * kBwdKvBN;
@@ -394,19 +407,20 @@ __device__ __forceinline__ QStep q_advance(const int32_t *items, QStep s, int fi
 }
 
 template <int D, typename InT, typename GT>
-__global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D> &sm) {
   using C = BwdCfg<D>;
   constexpr int BN = kBwdQBN;  // 64 keys per tile
   constexpr int NS = kBwdQStages;
   constexpr int BUF = 2 * C::TSZ;  // K (column layout, read both ways), V (row layout)
-  __shared__ __attribute__((aligned(16))) __bf16 lds[NS * BUF];
+  static_assert(NS * BUF == BwdSmem<D>::kRing, "backward LDS layout");
+  __bf16 *lds = sm.ring;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
 
   int rank, h;
-  map_head(blockIdx.x, a.hq, rank, h);
+  map_head(x, a.hq, rank, h);
   const int32_t *__restrict__ items = a.items;
   const float *__restrict__ lse = a.lse;
   const float *__restrict__ delta = a.delta;
@@ -585,17 +599,29 @@ __global__ __launch_bounds__(64 * kBwdQWaves) void dq_kernel(BwdArgs a) {
   }
 }
 
+// One launch for both roles: workgroups [0, kv_blocks) are dK/dV tiles,
+// [kv_pad, kv_pad + q blocks) dQ tiles (kv_pad = kv_blocks rounded up to a
+// multiple of the 8 XCDs so that both parts keep the head -> XCD map; the
+// padding workgroups exit at once).  dQ workgroups start as the dK/dV ones
+// drain, filling the tail of the longer part.
 template <int D, typename InT, typename GT>
-static hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.n_kv_units * a.hkv;
-  hipLaunchKernelGGL((dkdv_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0, s, a);
-  return hipGetLastError();
+__global__ __launch_bounds__(64 * kBwdKvWaves) void bwd_kernel(BwdArgs a) {
+  static_assert(kBwdKvWaves == kBwdQWaves, "both roles use the same workgroup size");
+  __shared__ __attribute__((aligned(16))) __bf16 ring[BwdSmem<D>::kRing];
+  __shared__ __attribute__((aligned(16))) float stat[kBwdKvStages][2][kBwdKvBM];
+  __shared__ __attribute__((aligned(16))) uint32_t pshare[4][2][2][64][4];
+  const BwdSmem<D> sm{ring, stat, pshare};
+  const int x = blockIdx.x;
+  if (x < a.kv_blocks)
+    dkdv_body<D, InT, GT>(a, x, sm);
+  else if (x >= a.kv_pad)
+    dq_body<D, InT, GT>(a, x - a.kv_pad, sm);
 }
 
 template <int D, typename InT, typename GT>
-static hipError_t launch_dq_t(const BwdArgs &a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.n_q_units * a.hq;
-  hipLaunchKernelGGL((dq_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdQWaves), 0, s, a);
+static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.kv_pad + (int64_t)a.n_q_units * a.hq;
+  hipLaunchKernelGGL((bwd_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -612,12 +638,8 @@ static hipError_t launch_dq_t(const BwdArgs &a, hipStream_t s) {
     return gb ? dev::FN<64, float, __bf16>(a, s) : dev::FN<64, float, float>(a, s);       \
   } while (0)
 
-hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
-  SEGATTN_DISPATCH(launch_dkdv_t, a, d, in_dtype, g_dtype, s);
-}
-
-hipError_t launch_bwd_dq(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
-  SEGATTN_DISPATCH(launch_dq_t, a, d, in_dtype, g_dtype, s);
+hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
+  SEGATTN_DISPATCH(launch_bwd_t, a, d, in_dtype, g_dtype, s);
 }
 
 #undef SEGATTN_DISPATCH

@@ -73,6 +73,8 @@ struct BwdArgs {
   const int32_t *items, *kvg, *qg;
   int32_t n_items, n_kvg, n_qg;
   int32_t n_kv_units, n_q_units;
+  int32_t kv_blocks;     // n_kv_units * hkv: dK/dV workgroups
+  int32_t kv_pad;        // kv_blocks rounded up to a multiple of 8: first dQ workgroup
   int64_t tokens;
   int32_t hq, hkv;
   float scale, scale_log2;
@@ -91,8 +93,7 @@ struct MergeArgs {
 // resolved inside the .hip files from the runtime dtype codes.
 hipError_t launch_fwd(const FwdArgs &a, int d, int in_dtype, int o_dtype, hipStream_t s);
 hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 // Copies n int32 words from host memory into dst (device) through kernel
 // arguments: stream-ordered, graph-capturable, no pageable-memory copy.

@@ -85,14 +85,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
 }
 
 // ---------------------------------------------------------------- upload
-constexpr int kUploadWords = 248;
+constexpr int kUploadWords = 1000;  // 4 KB of kernel arguments per launch
 struct UploadChunk {
   int32_t n;
   int32_t pad;
   int32_t w[kUploadWords];
 };
 
-__global__ __launch_bounds__(256) void upload_kernel(int32_t *dst, UploadChunk c) {
+__global__ __launch_bounds__(1024) void upload_kernel(int32_t *dst, UploadChunk c) {
   const int i = threadIdx.x;
   if (i < c.n) dst[i] = c.w[i];
 }
@@ -137,7 +137,7 @@ hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStrea
     c.n = (int32_t)((n - off) < kUploadWords ? (n - off) : kUploadWords);
     c.pad = 0;
     for (int i = 0; i < c.n; ++i) c.w[i] = words[off + i];
-    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, dst + off, c);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(1024), 0, s, dst + off, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
