@@ -277,16 +277,24 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem
         for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
           for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
+      pipelined<2 * C::KS>(
+          [&](auto ic) __attribute__((always_inline)) {
+            constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+            struct {
+              bf16x8 f[2];
+            } xa;
 #pragma unroll
-      for (int qp = 0; qp < 2; ++qp)
+            for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+            return xa;
+          },
+          [&](auto ic, const auto &xa) __attribute__((always_inline)) {
+            constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
+            for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            const bf16x8 xa = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
-#pragma unroll
-            for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = mfma16(xa, xf[nk][ks], x[qp][ab][nk]);
-          }
+              for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], x[qp][ab][nk]);
+          });
       if (!dk_role) {
         // Rows past q_hi of a partial tile repeat the last row in LDS and
         // must drop out here too.
@@ -350,14 +358,24 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem
         }
       }
       const __bf16 *Bt = dk_role ? Qs : dOs;
+      // sub-step nt: the transposed fragments of head-dim block nt, both halves
+      pipelined<C::NT>(
+          [&](auto ntc) __attribute__((always_inline)) {
+            constexpr int nt = decltype(ntc)::value;
+            struct {
+              bf16x8 f[2];
+            } bt;
 #pragma unroll
-      for (int qp = 0; qp < 2; ++qp)
+            for (int qp = 0; qp < 2; ++qp) bt.f[qp] = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
+            return bt;
+          },
+          [&](auto ntc, const auto &bt) __attribute__((always_inline)) {
+            constexpr int nt = decltype(ntc)::value;
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-          const bf16x8 bt = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
+            for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt, acc[nk][nt]);
-        }
+              for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt.f[qp], acc[nk][nt]);
+          });
     }
     cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
     ++done;
@@ -530,18 +548,30 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D
             s[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
             dp[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
           }
+        // sub-step ks: the K and V row fragments of depth step ks
+        pipelined<C::KS>(
+            [&](auto ksc) __attribute__((always_inline)) {
+              constexpr int ks = decltype(ksc)::value;
+              struct {
+                bf16x8 k[2], v[2];
+              } f;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
+              for (int ab = 0; ab < 2; ++ab) {
+                f.k[ab] = lds_row8(Ks, rkoff[ks] + (32 * kp + 4 * ab) * 2 * D);
+                f.v[ab] = lds_row8(Vs, rvoff[ks] + (32 * kp + 4 * ab) * 2 * D);
+              }
+              return f;
+            },
+            [&](auto ksc, const auto &f) __attribute__((always_inline)) {
+              constexpr int ks = decltype(ksc)::value;
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            const bf16x8 ka = lds_row8(Ks, rkoff[ks] + (32 * kp + 4 * ab) * 2 * D);
-            const bf16x8 va = lds_row8(Vs, rvoff[ks] + (32 * kp + 4 * ab) * 2 * D);
+              for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-            for (int nq = 0; nq < 2; ++nq) {
-              s[nq][ab] = mfma16(ka, qf[nq][ks], s[nq][ab]);
-              dp[nq][ab] = mfma16(va, dof[nq][ks], dp[nq][ab]);
-            }
-          }
+                for (int nq = 0; nq < 2; ++nq) {
+                  s[nq][ab] = mfma16(f.k[ab], qf[nq][ks], s[nq][ab]);
+                  dp[nq][ab] = mfma16(f.v[ab], dof[nq][ks], dp[nq][ab]);
+                }
+            });
         // dS = P (dP - D); the masked variant is a separate code path so
         // that interior tiles carry no per-element compares.
         auto make_ds = [&](auto maskc) __attribute__((always_inline)) {
@@ -569,14 +599,24 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D
           make_ds(std::false_type{});
       }
       // ---- dQ^T += K^T dS^T
+      // sub-step nt: the transposed K fragments of head-dim block nt
+      pipelined<C::NT>(
+          [&](auto ntc) __attribute__((always_inline)) {
+            constexpr int nt = decltype(ntc)::value;
+            struct {
+              bf16x8 f[2];
+            } ka;
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
+            for (int kp = 0; kp < 2; ++kp) ka.f[kp] = lds_col8<D>(Ks, coff[nt] + 32 * kp * 2 * D);
+            return ka;
+          },
+          [&](auto ntc, const auto &ka) __attribute__((always_inline)) {
+            constexpr int nt = decltype(ntc)::value;
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          const bf16x8 ka = lds_col8<D>(Ks, coff[nt] + 32 * kp * 2 * D);
+            for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-          for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka, dsb[nq][kp], dq[nq][nt]);
-        }
+              for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka.f[kp], dsb[nq][kp], dq[nq][nt]);
+          });
     }
     cp = q_advance(items, cp, first, r1);
     ++done;

@@ -195,17 +195,28 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
           s[nq][kp][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
           s[nq][kp][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
+      // sub-step ks: the 2 x KP key fragments of depth step ks
+      pipelined<C::KS>(
+          [&](auto ksc) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ksc)::value;
+            struct {
+              bf16x8 f[C::KP][2];
+            } kf;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+            for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
-        for (int kp = 0; kp < C::KP; ++kp)
+              for (int ab = 0; ab < 2; ++ab) kf.f[kp][ab] = lds_row8(Ks, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
+            return kf;
+          },
+          [&](auto ksc, const auto &kf) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ksc)::value;
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab) {
-            const bf16x8 kf = lds_row8(Ks, roff[ks] + (32 * kp + 4 * ab) * 2 * D);
+            for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
-            for (int nq = 0; nq < C::NQ; ++nq) s[nq][kp][ab] = mfma16(kf, qf[nq][ks], s[nq][kp][ab]);
-          }
-      }
+              for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                for (int nq = 0; nq < C::NQ; ++nq) s[nq][kp][ab] = mfma16(kf.f[kp][ab], qf[nq][ks], s[nq][kp][ab]);
+          });
 
       // ---- masking (boundary tiles only: a separate code path, so that
       // interior tiles carry no per-element compares)
@@ -268,14 +279,24 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
       }
 
       // ---- O^T += V^T P^T
+      // sub-step mt: the V^T fragments of head-dim block mt
+      pipelined<C::MT>(
+          [&](auto mtc) __attribute__((always_inline)) {
+            constexpr int mt = decltype(mtc)::value;
+            struct {
+              bf16x8 f[C::KP];
+            } vf;
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+            for (int kp = 0; kp < C::KP; ++kp) vf.f[kp] = lds_col8<D>(Vs, coff[mt] + 32 * kp * 2 * D);
+            return vf;
+          },
+          [&](auto mtc, const auto &vf) __attribute__((always_inline)) {
+            constexpr int mt = decltype(mtc)::value;
 #pragma unroll
-        for (int kp = 0; kp < C::KP; ++kp) {
-          const bf16x8 vf = lds_col8<D>(Vs, coff[mt] + 32 * kp * 2 * D);
+            for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
-          for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf, pf[nq][kp], o[nq][mt]);
-        }
+              for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf.f[kp], pf[nq][kp], o[nq][mt]);
+          });
     }
     ++j;
     return j < ntiles;

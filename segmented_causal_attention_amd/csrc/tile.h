@@ -203,6 +203,28 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   wait_vm<0>();
 }
 
+// Software pipeline over N unrolled sub-steps: the operands of sub-step i+1
+// are loaded (load(ic<i+1>)) before sub-step i consumes its own
+// (use(ic<i>, ops)), so LDS latency overlaps the matrix products instead of
+// stalling before each group of them.
+template <int I, int N, typename L, typename U, typename T>
+__device__ __forceinline__ void pipe_step(L &load, U &use, const T &cur) {
+  if constexpr (I + 1 < N) {
+    const auto nxt = load(std::integral_constant<int, I + 1>{});
+    // keep the compiler's scheduler from sinking those loads below the
+    // products that follow
+    __builtin_amdgcn_sched_barrier(0);
+    use(std::integral_constant<int, I>{}, cur);
+    pipe_step<I + 1, N>(load, use, nxt);
+  } else {
+    use(std::integral_constant<int, I>{}, cur);
+  }
+}
+template <int N, typename L, typename U>
+__device__ __forceinline__ void pipelined(L load, U use) {
+  pipe_step<0, N>(load, use, load(std::integral_constant<int, 0>{}));
+}
+
 // Runs f(integral_constant<B>) for B = 0 .. NS-1 while it returns true; the
 // ring slot of every step is a compile-time constant.
 template <int B, int NS, typename F>
