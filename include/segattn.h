@@ -157,8 +157,8 @@ int segattn_fwd(const segattn_shape *shape, const void *q, const void *k, const 
  * o_*: device float [rows][h][d]; lse_*: device float, element (hh, r) at
  * lse[hh * lse_stride + r] (lse_stride >= rows, e.g. the full token count
  * when merging a row range of a larger tensor).  o_out/lse_out may alias
- * the a or b operands exactly (in place).  Errors: E_INVALID, E_RANGE,
- * E_DEVICE. */
+ * the a or b operands exactly (in place).  d: a multiple of 4, at most 1024.
+ * Errors: E_INVALID, E_UNSUPPORTED (d > 1024), E_RANGE, E_DEVICE. */
 int segattn_merge(int64_t rows, int32_t h, int32_t d, int64_t lse_stride,
                   const float *o_a, const float *lse_a, const float *o_b, const float *lse_b,
                   float *o_out, float *lse_out, void *stream);

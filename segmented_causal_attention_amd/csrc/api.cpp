@@ -293,6 +293,7 @@ extern "C" int segattn_merge(int64_t rows, int32_t h, int32_t d, int64_t lse_str
   clear_error();
   static const char *fn = "segattn_merge";
   if (rows < 1 || h < 1 || d < 4 || d % 4) return fail(SEGATTN_E_INVALID, "%s: rows, h >= 1 and d a multiple of 4", fn);
+  if (d > 1024) return fail(SEGATTN_E_UNSUPPORTED, "%s: d = %d > 1024", fn, d);
   if (lse_stride < rows) return fail(SEGATTN_E_INVALID, "%s: lse_stride < rows", fn);
   if (rows > (int64_t)1 << 40 || (int64_t)h * lse_stride > (int64_t)1 << 40)
     return fail(SEGATTN_E_RANGE, "%s: sizes too large", fn);

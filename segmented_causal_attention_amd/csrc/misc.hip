@@ -12,32 +12,85 @@ namespace dev {
 //   m = max(l_a, l_b);  m = -inf -> (0, -inf);  w = e^(l - m);
 //   LSE = m + log(w_a + w_b),  O = (w_a O_a + w_b O_b) / (w_a + w_b).
 // One thread per 4 consecutive floats of a (row, head) vector; the d/4
-// threads of one vector sit in one wavefront, so an in-place merge reads the
-// old LSE in every lane before any lane stores the new one.
+// threads of one vector sit in one wavefront, which issues all its loads
+// before any store, so an in-place merge reads the old LSE in every lane
+// before a lane overwrites it.  A workgroup takes kMergeUnroll groups of
+// 256/(d/4) consecutive vectors with all their loads in flight at once; the
+// only 64-bit division is one per workgroup.
+constexpr int kMergeUnroll = 4;
+
+__device__ __forceinline__ void merge_one(const MergeArgs &a, int64_t vec, int64_t li, int c, const f32x4 &oa,
+                                          const f32x4 &ob, float la, float lb) {
+  const float m = fmaxf(la, lb);
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  float lse = kNegInf;
+  if (m != kNegInf) {
+    const float wa = fast_exp2((la - m) * kLog2e), wb = fast_exp2((lb - m) * kLog2e);
+    const float den = wa + wb, inv = 1.f / den;
+    out = oa * (wa * inv) + ob * (wb * inv);
+    lse = m + fast_log2(den) * kLn2;
+  }
+  *reinterpret_cast<f32x4 *>(a.o_out + vec * a.d + 4 * c) = out;
+  if (c == 0) a.lse_out[li] = lse;
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int cpv = a.d >> 2;  // float4 chunks per (row, head) vector
-  const int64_t total = a.rows * a.h * cpv;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    const int64_t vec = idx / cpv;
-    const int c = (int)(idx - vec * cpv);
-    const int64_t r = vec / a.h;
-    const int hh = (int)(vec - r * a.h);
-    const int64_t li = (int64_t)hh * a.lse_stride + r;
-    const float la = a.lse_a[li], lb = a.lse_b[li];
-    const float m = fmaxf(la, lb);
-    const f32x4 oa = *reinterpret_cast<const f32x4 *>(a.o_a + vec * a.d + 4 * c);
-    const f32x4 ob = *reinterpret_cast<const f32x4 *>(a.o_b + vec * a.d + 4 * c);
-    f32x4 out = {0.f, 0.f, 0.f, 0.f};
-    float lse = kNegInf;
-    if (m != kNegInf) {
-      const float wa = fast_exp2((la - m) * kLog2e), wb = fast_exp2((lb - m) * kLog2e);
-      const float den = wa + wb, inv = 1.f / den;
-      out = oa * (wa * inv) + ob * (wb * inv);
-      lse = m + fast_log2(den) * kLn2;
+  constexpr int CPV = D / 4, VPB = 256 / CPV, U = kMergeUnroll;
+  const int tid = threadIdx.x, c = tid % CPV, vl = tid / CPV;
+  const int64_t nvec = a.rows * a.h;
+  const int64_t nblk = (nvec + VPB * U - 1) / (VPB * U);
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+  const int64_t vbase = blk * (VPB * U);
+  const int64_t r0 = vbase / a.h;
+  const int hh0 = (int)(vbase - r0 * a.h);
+  f32x4 oa[U], ob[U];
+  float la[U], lb[U];
+  int64_t li[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = u * VPB + vl;
+    const int t = hh0 + v;
+    const int64_t vec = vbase + v;
+    li[u] = (int64_t)(t % a.h) * a.lse_stride + r0 + t / a.h;
+    if (vec < nvec) {
+      oa[u] = *reinterpret_cast<const f32x4 *>(a.o_a + vec * D + 4 * c);
+      ob[u] = *reinterpret_cast<const f32x4 *>(a.o_b + vec * D + 4 * c);
+      la[u] = a.lse_a[li[u]];
+      lb[u] = a.lse_b[li[u]];
     }
-    *reinterpret_cast<f32x4 *>(a.o_out + vec * a.d + 4 * c) = out;
-    if (c == 0) a.lse_out[li] = lse;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t vec = vbase + u * VPB + vl;
+    if (vec < nvec) merge_one(a, vec, li[u], c, oa[u], ob[u], la[u], lb[u]);
+  }
+  }
+}
+
+// Any other d (a multiple of 4, at most 1024): a workgroup takes whole
+// vectors, 256/(d/4) of them per pass, so all threads of a vector load
+// before a barrier and store after it (in-place safe).
+__global__ __launch_bounds__(256) void merge_kernel_any(MergeArgs a) {
+  const int cpv = a.d >> 2, vpb = 256 / cpv;
+  const int tid = threadIdx.x, vl = tid / cpv, c = tid - vl * cpv;
+  const int64_t nvec = a.rows * a.h;
+  for (int64_t vb = (int64_t)blockIdx.x * vpb; vb < nvec; vb += (int64_t)gridDim.x * vpb) {
+    const int64_t vec = vb + vl;
+    const bool ok = vl < vpb && vec < nvec;
+    const int64_t r = ok ? vec / a.h : 0;
+    const int64_t li = ok ? (vec - r * a.h) * a.lse_stride + r : 0;
+    f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = oa;
+    float la = kNegInf, lb = kNegInf;
+    if (ok) {
+      oa = *reinterpret_cast<const f32x4 *>(a.o_a + vec * a.d + 4 * c);
+      ob = *reinterpret_cast<const f32x4 *>(a.o_b + vec * a.d + 4 * c);
+      la = a.lse_a[li];
+      lb = a.lse_b[li];
+    }
+    __syncthreads();
+    if (ok) merge_one(a, vec, li, c, oa, ob, la, lb);
+    __syncthreads();
   }
 }
 
@@ -108,8 +161,14 @@ static unsigned grid_for(int64_t work, int64_t per_block) {
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
   using namespace dev;
-  const int64_t work = a.rows * a.h * (a.d / 4);
-  hipLaunchKernelGGL(merge_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s, a);
+  const int64_t nvec = a.rows * a.h;
+  if (a.d == 128) {
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid_for(nvec, (256 / 32) * kMergeUnroll)), dim3(256), 0, s, a);
+  } else if (a.d == 64) {
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid_for(nvec, (256 / 16) * kMergeUnroll)), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(merge_kernel_any, dim3(grid_for(nvec, 256 / (a.d / 4))), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -237,5 +237,6 @@ def test_merge_argument_errors():
     assert L.segattn_merge(0, 1, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert L.segattn_merge(8, 1, 126, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert L.segattn_merge(8, 1, 128, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.segattn_merge(8, 1, 1028, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.SEGATTN_E_UNSUPPORTED
     assert L.segattn_merge(8, 1, 128, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert L.segattn_merge(8, 1, 128, 8, FAKE, ctypes.c_void_p(0x1001), FAKE, FAKE, FAKE, FAKE, None) == 1

@@ -124,6 +124,32 @@ def test_merge_kernel_in_and_out_of_place():
     assert np.array_equal(host64(A2[:r0]), oa[:r0].double().numpy())
 
 
+@pytest.mark.parametrize("rows,h,d", [(1000, 5, 64), (77, 5, 12), (130, 3, 1024)])
+def test_merge_kernel_other_head_dims(rows, h, d):
+    """The d = 64 fast path and the generic path (any multiple of 4), in and
+    out of place, with empty (-inf) rows on either side."""
+    say(f"case merge rows={rows} h={h} d={d}")
+    g = torch.Generator(device="cpu").manual_seed(rows + d)
+    oa = torch.randn((rows, h, d), generator=g, dtype=torch.float32)
+    ob = torch.randn((rows, h, d), generator=g, dtype=torch.float32)
+    la = torch.randn((h, rows), generator=g) * 3
+    lb = torch.randn((h, rows), generator=g) * 3
+    la[0, :10] = -math.inf
+    lb[0, 5:20] = -math.inf
+    oa[:10, 0] = 0
+    ob[5:20, 0] = 0
+    ro, rl = oracle.merge(oa.numpy(), la.numpy(), ob.numpy(), lb.numpy())
+    A, LA, Bo, LB = (x.to(DEV) for x in (oa, la, ob, lb))
+    o, l = sa.segattn_merge(A, LA, Bo, LB)
+    torch.cuda.synchronize()
+    assert_close_o(o, ro, "O")
+    assert_close_o(l, rl, "LSE")
+    sa.segattn_merge(A, LA, Bo, LB, o_out=Bo, lse_out=LB)  # in place into b
+    torch.cuda.synchronize()
+    assert_close_o(Bo, ro, "O in place")
+    assert_close_o(LB, rl, "LSE in place")
+
+
 def test_indexing_probe_zero_keys():
     """K = 0 makes every visible score exactly 0, so LSE_q = ln(count_q) where
     count_q is the number of keys the item lets row q see; exp(LSE) rounds
