@@ -34,6 +34,41 @@ import numpy as np
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # CUs x clock x dense bf16 FLOP/clk/CU = 2516.6
 PEAK_HBM_GBS = 8000.0
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+# The device code; counter readings taken on other sources are not reported.
+KERNEL_SOURCES = ("fwd.hip", "bwd.hip", "misc.hip", "tile.h", "device_common.h", "kernels.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "segmented_causal_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload`, as recorded in
+    profiles/traffic_<kernel>_<workload>.md from two rocprofv3 counter runs
+    (FETCH_SIZE, WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when there is no record or the kernel sources changed since."""
+    path = os.path.join(HERE, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+            if len(cells) == 2:
+                fields[cells[0]] = cells[1]
+    if fields.get("kernel sources sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -188,7 +223,9 @@ def hbm_kernels(torch, sa, W):
                 place: (3 * 4 * d + 12) bytes per (row, head);
       D      -- the backward reduction D = <dO, O> of this workload
                 (segattn_bwd_preprocess): (2 * 2 * d + 4) bytes per (row, head)
-                for bf16 O and dO."""
+                for bf16 O and dO;
+      copy   -- a plain 2 GiB device-to-device copy (torch), the reference
+                for what streaming reaches and for the HBM counters."""
     E = torch.cuda.Event
 
     def timed(fn, n=10):
@@ -217,6 +254,16 @@ def hbm_kernels(torch, sa, W):
                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
                     "ms": round(ms, 4), "bytes": nbytes, "shape": [rows, h, d]}
     del oa, ob, la, lb, oo, lo
+    # plain device copy of 2 GiB (read + write): what streaming reaches on
+    # this GPU, and the known-size kernel that calibrates the HBM counters
+    src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    nbytes = 2 * src.numel() * 4
+    out["copy_reference"] = {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "ms": round(ms, 4), "bytes": nbytes}
+    del src, dst
     rev = W.items[::-1].copy()
     ms = timed(lambda: sa.segattn_bwd_preprocess(W.q, W.k, W.o, W.do, rev, W.bws))
     nbytes = ((W.o.element_size() + W.do.element_size()) * W.d + 4) * W.T * W.hq
@@ -267,9 +314,9 @@ def main():
     # whichever takes longer per step; ring workloads launch the forward once
     # per ring step, and the reported time is their sum.
     if bwd_ms >= fwd_ms:
-        dom, dom_ms, dom_flops = "bwd_kernel (segattn_bwd)", bwd_ms, W.flops_bwd
+        dom, dom_ms, dom_flops, tag = "bwd_kernel (segattn_bwd)", bwd_ms, W.flops_bwd, "bwd_kernel"
     else:
-        dom, dom_ms, dom_flops = "fwd_kernel (segattn_fwd)", fwd_ms, W.flops_fwd
+        dom, dom_ms, dom_flops, tag = "fwd_kernel (segattn_fwd)", fwd_ms, W.flops_fwd, "fwd_kernel"
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     out = {
         "metric": "segmented causal attn fwd+bwd TFLOP/s and % of bf16 MFMA peak, 1 GPU",
@@ -290,7 +337,8 @@ def main():
         "breakdown_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(tag, W.w["name"])},
     }
     if not args.no_hbm_kernels:
         out["hbm_kernels"] = hbm_kernels(torch, sa, W)

@@ -81,17 +81,6 @@ __device__ __forceinline__ int find_unit(const int32_t *tab, int words, int fiel
   return lo;
 }
 
-__device__ __forceinline__ void map_head(int x, int nh, int &rank, int &h) {
-  if ((nh & 7) == 0) {
-    const int hpx = nh >> 3, xcd = x & 7, j = x >> 3;
-    rank = j / hpx;
-    h = xcd * hpx + j % hpx;
-  } else {
-    rank = x / nh;
-    h = x % nh;
-  }
-}
-
 // =================================================================== dK/dV
 
 struct KvStep {
@@ -159,7 +148,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem
   const bool dk_role = wave >= NG;
 
   int rank, g;
-  map_head(x, a.hkv, rank, g);
+  map_xcd(x, a.hkv, a.n_kv_units, rank, g);
   const int32_t *kv = a.kvg + find_unit(a.kvg, 4, 3, a.n_kvg, rank) * 4;
   const int seq_off = kv[0], kb = kv[1], ke = kv[2];
   const int kt0 = kb + (rank - kv[3]) * kBwdKvBN;
@@ -438,7 +427,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D
   const int l16 = lane & 15, lg = lane >> 4;
 
   int rank, h;
-  map_head(x, a.hq, rank, h);
+  map_xcd(x, a.hq, a.n_q_units, rank, h);
   const int32_t *__restrict__ items = a.items;
   const float *__restrict__ lse = a.lse;
   const float *__restrict__ delta = a.delta;

@@ -104,6 +104,23 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v, const XorLanes &x) {
   return v;
 }
 
+// Workgroup index -> (unit rank, head) for a grid of nunits x nh workgroups.
+// Consecutive workgroups are dealt to the 8 XCDs in turn.  When nh is a
+// multiple of 8, XCD c takes the heads [c*nh/8, (c+1)*nh/8) one after the
+// other, each head's units in rank (heaviest-first) order, so the
+// workgroups resident on one XCD at a time mostly belong to one head and
+// stream the same tiles through that XCD's L2.
+__device__ __forceinline__ void map_xcd(int x, int nh, int nunits, int &rank, int &h) {
+  if ((nh & 7) == 0) {
+    const int xcd = x & 7, j = x >> 3;
+    h = xcd * (nh >> 3) + j / nunits;
+    rank = j - (j / nunits) * nunits;
+  } else {
+    rank = x / nh;
+    h = x - rank * nh;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

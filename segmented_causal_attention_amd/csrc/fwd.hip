@@ -41,21 +41,6 @@ struct FwdCfg {
 };
 static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * 32, "forward tile shape");
 
-// Workgroup index -> (tile rank, head).  Consecutive workgroups go to the 8
-// XCDs in turn; when hq is a multiple of 8, XCD c gets the heads
-// [c*hq/8, (c+1)*hq/8) so the workgroups sharing an XCD's L2 read the same
-// K/V, while every XCD still receives the tile ranks heaviest-first.
-__device__ __forceinline__ void map_unit(int x, int hq, int &rank, int &h) {
-  if ((hq & 7) == 0) {
-    const int hpx = hq >> 3, xcd = x & 7, j = x >> 3;
-    rank = j / hpx;
-    h = xcd * hpx + j % hpx;
-  } else {
-    rank = x / hq;
-    h = x % hq;
-  }
-}
-
 // Index of the item whose unit range holds `rank` (unit_begin ascending).
 __device__ __forceinline__ int find_item(const int32_t *items, int n, int rank) {
   int lo = 0, hi = n - 1;
@@ -92,7 +77,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
   const XorLanes xl(lane);
 
   int rank, h;
-  map_unit(blockIdx.x, a.hq, rank, h);
+  map_xcd(blockIdx.x, a.hq, a.n_units, rank, h);
   const int32_t *it = a.items + find_item(a.items, a.n_items, rank) * kItemWords;
   const int seq_off = it[0], q_lo = it[1], q_hi = it[2], k_lo = it[3], k_hi = it[4];
   const int tile = rank - it[5];
