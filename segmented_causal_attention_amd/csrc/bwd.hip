@@ -110,40 +110,46 @@ __device__ __forceinline__ KvStep kv_advance(const int32_t *items, KvStep s, int
   return kv_first_from(items, s.item - 1, seq_off, kt0, kt1);
 }
 
-// LDS of the backward kernel, shared by its two roles: the 64-row tile ring
-// (both roles), and for the dK/dV role the staged row statistics and the
-// P hand-over buffer.
+// LDS of the backward kernel.  Each role carves the same block its own way:
+//   dK/dV role: a ring of kBwdKvStages (Q, dO) 64-row tile pairs, their row
+//     statistics, and as many P hand-over buffers;
+//   dQ role:    a ring of kBwdQStages (K, V) 64-key tile pairs.
 template <int D>
-struct BwdSmem {
-  static constexpr int kRing = kBwdKvStages * 2 * kTileRows * D;  // bf16 elements
-  __bf16 *ring;
-  float (*stat)[2][kBwdKvBM];                      // [stage][LSE | D][row]
-  uint32_t (*pshare)[2][2][64][4];                 // [group][half][key block][lane] x 4 dwords
+struct BwdLds {
+  static constexpr int kTile = kTileRows * D;                     // bf16 elements of one tile
+  static constexpr int kKvRing = kBwdKvStages * 2 * kTile * 2;    // bytes
+  static constexpr int kKvStat = kBwdKvStages * 2 * kBwdKvBM * 4;
+  static constexpr int kKvP = kBwdKvStages * 4 * 2 * 2 * 64 * 16;  // [stage][group][half][key block][lane] x 16 B
+  static constexpr int kKv = kKvRing + kKvStat + kKvP;
+  static constexpr int kQ = kBwdQStages * 2 * kTile * 2;
+  static constexpr int kBytes = kKv > kQ ? kKv : kQ;
 };
 
 template <int D, typename InT, typename GT>
-__device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem<D> &sm) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   using C = BwdCfg<D>;
+  using L = BwdLds<D>;
   constexpr int W = kBwdKvWaves;
   constexpr int NG = W / 2;        // key groups of 32 keys
   constexpr int BQ = kBwdKvBM;     // 64 query rows per tile
   constexpr int NS = kBwdKvStages;
   constexpr int BUF = 2 * C::TSZ;  // Q, dO (column layout, read both ways)
-  static_assert(NS * BUF == BwdSmem<D>::kRing && NG == 4, "backward LDS layout");
-  __bf16 *lds = sm.ring;
-  float(*stat)[2][BQ] = sm.stat;
-  // P of the current tile, handed from each group's dV wavefront to its dK
-  // wavefront: [group][32-row half][16-key block][lane] x 8 bf16 values (the
-  // very operand of dV += P^T dO; bf16 keeps fp32's exponent range, which
-  // matters at a million keys where P ~ 1e-6 would be subnormal in fp16).
-  uint32_t(*pshare)[2][2][64][4] = sm.pshare;
+  static_assert(NG == 4 && BUF == 2 * L::kTile, "backward LDS layout");
+  __bf16 *lds = reinterpret_cast<__bf16 *>(smem);
+  float(*stat)[2][BQ] = reinterpret_cast<float(*)[2][BQ]>(smem + L::kKvRing);
+  // P of a tile, handed from each group's dV wavefront to its dK wavefront:
+  // [stage][group][32-row half][16-key block][lane] x 8 bf16 values (the very
+  // operand of dV += P^T dO; bf16 keeps fp32's exponent range, which matters
+  // at a million keys where P ~ 1e-6 would be subnormal in fp16).
+  uint32_t(*pshare)[NG][2][2][64][4] = reinterpret_cast<uint32_t(*)[NG][2][2][64][4]>(smem + L::kKvRing + L::kKvStat);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   // Wavefronts w and w + NG share key group w % NG (and a SIMD): the first
   // computes P and accumulates dV, the second computes dP, takes P from the
-  // first through LDS, and accumulates dK.
+  // first through LDS, and accumulates dK -- one query tile behind, so that
+  // the two never wait for each other inside a tile.
   const int kgrp = wave % NG;
   const bool dk_role = wave >= NG;
 
@@ -218,157 +224,152 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, const BwdSmem
   };
 
   const float c2 = a.scale_log2;
-  // Two walkers over the same step sequence: `ld` stages NS-1 steps ahead of
-  // `cp`, which is computed.
+  // Three walkers over the same step sequence: `ld` (staged), `cp` (the dV
+  // wavefronts' step) and `pk` (the dK wavefronts' step, one behind).
+  // Iteration i: stage i is published; stage i+1 is copied into the slot
+  // that step i-2 used (finished by both roles); the dV wavefronts work on
+  // step i in slot i % NS and hand P over in buffer i % NS; the dK
+  // wavefronts work on step i-1 in slot (i-1) % NS with its P.
   KvStep cp = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
+  KvStep pk{-1, 0, 0};
   KvStep ld = cp;
-  int issued = 0, done = 0;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (ld.item >= 0) {
-      stage(ld, s);
-      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
-      ++issued;
-    }
-  // One query tile in two phases separated by a barrier:
-  //   A: dV role  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS (bf16);
-  //      dK role  dP = dO V^T.
-  //   B: dV role  dV += P^T dO;
-  //      dK role  dS = P (dP - D) with P from LDS, dK += dS^T Q.
+  if (ld.item >= 0) {
+    stage(ld, 0);
+    ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+  }
   // Rows: half qp, sub-block ab of a 32-row half reads query rows
   // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of a half are the rows
   // 32qp + 8*lg + 0..7 for its key 16nk + l16 -- the A operand layout of the
-  // contraction over query rows.  The ring slot is a compile-time constant so
-  // every LDS read is a precomputed lane offset plus an immediate.
+  // contraction over query rows.  Slots are compile-time constants so every
+  // LDS read is a precomputed lane offset plus an immediate.
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
-    constexpr int buf = decltype(slot)::value;
-    wait_stages<2 * Loader::kInstr, NS>(issued - done - 1);
-    __syncthreads();  // stage `buf` visible; the slot staged next is free
+    constexpr int bv = decltype(slot)::value;  // dV role: step i
+    constexpr int bk = (bv + NS - 1) % NS;     // dK role: step i-1
+    wait_vm<0>();
+    __syncthreads();  // stage i visible; P of step i-1 visible; slot (i+1) % NS free
     if (ld.item >= 0) {
-      stage(ld, (buf + NS - 1) % NS);
+      stage(ld, (bv + 1) % NS);
       ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
-      ++issued;
     }
-    const int32_t *it = items + cp.item * kItemWords;
-    const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
-    const int qt0 = cp.qt0;
-    const int qt1 = min(qt0 + BQ, q_hi);
-    const bool active = has_keys && kw0 < qt1;
-    const __bf16 *Qs = lds + buf * BUF, *dOs = Qs + C::TSZ;
-    const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows of the phase-A product
-    bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
-    f32x4 x[2][2][2];                       // [qp][ab][nk]: S or dP
-    // ---------------------------------------------------------- phase A
-    if (active) {
+    const KvStep st = dk_role ? pk : cp;
+    if (st.item >= 0) {
+      const int32_t *it = items + st.item * kItemWords;
+      const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
+      const int qt0 = st.qt0;
+      const int qt1 = min(qt0 + BQ, q_hi);
+      if (has_keys && kw0 < qt1) {
+        const int b = dk_role ? bk : bv;
+        const __bf16 *Qs = lds + b * BUF, *dOs = Qs + C::TSZ;
+        const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows: S = Q K^T or dP = dO V^T
+        bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
+        f32x4 xs[2][2][2];                      // [qp][ab][nk]: S or dP
 #pragma unroll
-      for (int qp = 0; qp < 2; ++qp)
+        for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
-        for (int ab = 0; ab < 2; ++ab)
+          for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-          for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
-      pipelined<2 * C::KS>(
-          [&](auto ic) __attribute__((always_inline)) {
-            constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
-            struct {
-              bf16x8 f[2];
-            } xa;
+            for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
+        pipelined<2 * C::KS>(
+            [&](auto ic) __attribute__((always_inline)) {
+              constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+              struct {
+                bf16x8 f[2];
+              } xa;
 #pragma unroll
-            for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
-            return xa;
-          },
-          [&](auto ic, const auto &xa) __attribute__((always_inline)) {
-            constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+              for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+              return xa;
+            },
+            [&](auto ic, const auto &xa) __attribute__((always_inline)) {
+              constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
 #pragma unroll
-            for (int ab = 0; ab < 2; ++ab)
+              for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-              for (int nk = 0; nk < 2; ++nk) x[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], x[qp][ab][nk]);
-          });
-      if (!dk_role) {
-        // Rows past q_hi of a partial tile repeat the last row in LDS and
-        // must drop out here too.
-        const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
-        // The masked variant is a separate code path so that interior tiles
-        // carry no per-element compares.
-        auto make_p = [&](auto maskc) __attribute__((always_inline)) {
+                for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], xs[qp][ab][nk]);
+            });
+        if (!dk_role) {
+          // P = exp(S - LSE), masked on boundary tiles.  Rows past q_hi of a
+          // partial tile repeat the last row in LDS and must drop out too.
+          const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
+          // The masked variant is a separate code path so that interior
+          // tiles carry no per-element compares.
+          auto make_p = [&](auto maskc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qp = 0; qp < 2; ++qp) {
+              // -LSE in base 2 for rows 32qp + 8lg + 0..7
+              const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[bv][0][32 * qp + 8 * lg]) * -kLog2e;
+              const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[bv][0][32 * qp + 8 * lg + 4]) * -kLog2e;
+#pragma unroll
+              for (int nk = 0; nk < 2; ++nk) {
+                const int key = kw0 + 16 * nk + l16;
+                f32x4 pv[2];
+#pragma unroll
+                for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    float p = fast_exp2(fmaf(xs[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]));
+                    if constexpr (decltype(maskc)::value) {
+                      const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
+                      if (key > q || key < k_lo || key >= k_hi || q >= q_hi) p = 0.f;
+                    }
+                    pv[ab][i] = p;
+                  }
+                opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
+                *reinterpret_cast<bf16x8 *>(pshare[bv][kgrp][qp][nk][lane]) = opa[qp][nk];
+              }
+            }
+          };
+          if (need_mask)
+            make_p(std::true_type{});
+          else
+            make_p(std::false_type{});
+        } else {
+          // dS = P (dP - D) with the P the dV wavefront left one iteration ago
 #pragma unroll
           for (int qp = 0; qp < 2; ++qp) {
-            // -LSE in base 2 for rows 32qp + 8lg + 0..7
-            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg]) * -kLog2e;
-            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[buf][0][32 * qp + 8 * lg + 4]) * -kLog2e;
+            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg + 4]);
 #pragma unroll
             for (int nk = 0; nk < 2; ++nk) {
-              const int key = kw0 + 16 * nk + l16;
-              f32x4 pv[2];
+              const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk][kgrp][qp][nk][lane]);
+              f32x4 ds[2];
 #pragma unroll
               for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  float p = fast_exp2(fmaf(x[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]));
-                  if constexpr (decltype(maskc)::value) {
-                    const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
-                    if (key > q || key < k_lo || key >= k_hi || q >= q_hi) p = 0.f;
-                  }
-                  pv[ab][i] = p;
+                  const uint32_t w = ph[2 * ab + (i >> 1)];
+                  const float p = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+                  ds[ab][i] = p * (xs[qp][ab][nk][i] - (ab ? d1[i] : d0[i]));
                 }
-              opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
-              *reinterpret_cast<bf16x8 *>(pshare[kgrp][qp][nk][lane]) = opa[qp][nk];
+              opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
             }
           }
-        };
-        if (need_mask)
-          make_p(std::true_type{});
-        else
-          make_p(std::false_type{});
-      }
-    }
-    __syncthreads();
-    // ---------------------------------------------------------- phase B
-    if (active) {
-      if (dk_role) {
-#pragma unroll
-        for (int qp = 0; qp < 2; ++qp) {
-          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[buf][1][32 * qp + 8 * lg + 4]);
-#pragma unroll
-          for (int nk = 0; nk < 2; ++nk) {
-            const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[kgrp][qp][nk][lane]);
-            f32x4 ds[2];
-#pragma unroll
-            for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t w = ph[2 * ab + (i >> 1)];
-                const float p = (i & 1) ? bf16_hi(w) : bf16_lo(w);
-                ds[ab][i] = p * (x[qp][ab][nk][i] - (ab ? d1[i] : d0[i]));
-              }
-            opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
-          }
         }
+        // dV += P^T dO or dK += dS^T Q; sub-step nt: the transposed
+        // fragments of head-dim block nt, both halves
+        const __bf16 *Bt = dk_role ? Qs : dOs;
+        pipelined<C::NT>(
+            [&](auto ntc) __attribute__((always_inline)) {
+              constexpr int nt = decltype(ntc)::value;
+              struct {
+                bf16x8 f[2];
+              } bt;
+#pragma unroll
+              for (int qp = 0; qp < 2; ++qp) bt.f[qp] = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
+              return bt;
+            },
+            [&](auto ntc, const auto &bt) __attribute__((always_inline)) {
+              constexpr int nt = decltype(ntc)::value;
+#pragma unroll
+              for (int qp = 0; qp < 2; ++qp)
+#pragma unroll
+                for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt.f[qp], acc[nk][nt]);
+            });
       }
-      const __bf16 *Bt = dk_role ? Qs : dOs;
-      // sub-step nt: the transposed fragments of head-dim block nt, both halves
-      pipelined<C::NT>(
-          [&](auto ntc) __attribute__((always_inline)) {
-            constexpr int nt = decltype(ntc)::value;
-            struct {
-              bf16x8 f[2];
-            } bt;
-#pragma unroll
-            for (int qp = 0; qp < 2; ++qp) bt.f[qp] = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
-            return bt;
-          },
-          [&](auto ntc, const auto &bt) __attribute__((always_inline)) {
-            constexpr int nt = decltype(ntc)::value;
-#pragma unroll
-            for (int qp = 0; qp < 2; ++qp)
-#pragma unroll
-              for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt.f[qp], acc[nk][nt]);
-          });
     }
-    cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
-    ++done;
-    return cp.item >= 0;
+    pk = cp;
+    if (cp.item >= 0) cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
+    return pk.item >= 0;
   };
   if (cp.item >= 0)
     while (ring_pass<0, NS>(step)) {
@@ -414,13 +415,13 @@ __device__ __forceinline__ QStep q_advance(const int32_t *items, QStep s, int fi
 }
 
 template <int D, typename InT, typename GT>
-__device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D> &sm) {
+__device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   using C = BwdCfg<D>;
   constexpr int BN = kBwdQBN;  // 64 keys per tile
   constexpr int NS = kBwdQStages;
   constexpr int BUF = 2 * C::TSZ;  // K (column layout, read both ways), V (row layout)
-  static_assert(NS * BUF == BwdSmem<D>::kRing, "backward LDS layout");
-  __bf16 *lds = sm.ring;
+  static_assert(NS * BUF * 2 == BwdLds<D>::kQ, "backward LDS layout");
+  __bf16 *lds = reinterpret_cast<__bf16 *>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -636,15 +637,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, const BwdSmem<D
 template <int D, typename InT, typename GT>
 __global__ __launch_bounds__(64 * kBwdKvWaves) void bwd_kernel(BwdArgs a) {
   static_assert(kBwdKvWaves == kBwdQWaves, "both roles use the same workgroup size");
-  __shared__ __attribute__((aligned(16))) __bf16 ring[BwdSmem<D>::kRing];
-  __shared__ __attribute__((aligned(16))) float stat[kBwdKvStages][2][kBwdKvBM];
-  __shared__ __attribute__((aligned(16))) uint32_t pshare[4][2][2][64][4];
-  const BwdSmem<D> sm{ring, stat, pshare};
+  __shared__ __attribute__((aligned(16))) char smem[BwdLds<D>::kBytes];
   const int x = blockIdx.x;
   if (x < a.kv_blocks)
-    dkdv_body<D, InT, GT>(a, x, sm);
+    dkdv_body<D, InT, GT>(a, x, smem);
   else if (x >= a.kv_pad)
-    dq_body<D, InT, GT>(a, x - a.kv_pad, sm);
+    dq_body<D, InT, GT>(a, x - a.kv_pad, smem);
 }
 
 template <int D, typename InT, typename GT>

@@ -34,8 +34,10 @@ constexpr int kBwdKvBM = 64;
 constexpr int kBwdQWaves = 8;
 constexpr int kBwdQBM = 32 * kBwdQWaves;
 constexpr int kBwdQBN = 64;
-// Depth of the LDS prefetch rings (tiles in flight + the one in use).
-constexpr int kBwdKvStages = 4;
+// Depth of the LDS rings.  dK/dV role: the tile the dV wavefronts use, the
+// one the dK wavefronts (one step behind) use, and one in flight.  dQ role:
+// the tile in use and three in flight.
+constexpr int kBwdKvStages = 3;
 constexpr int kBwdQStages = 4;
 
 struct FwdArgs {
