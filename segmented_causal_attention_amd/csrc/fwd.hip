@@ -29,9 +29,9 @@ namespace dev {
 template <int D>
 struct FwdCfg {
   static constexpr int W = kFwdWaves;      // wavefronts per workgroup
-  static constexpr int BM = kFwdBM;        // query rows per workgroup (W x 32)
+  static constexpr int BM = kFwdBM;        // query rows per workgroup
   static constexpr int BN = kFwdBN;        // keys per LDS tile (= kTileRows)
-  static constexpr int NQ = 2;             // 16-row subtiles per wavefront (32 rows)
+  static constexpr int NQ = kFwdWaveRows / 16;  // 16-row subtiles per wavefront
   static constexpr int KS = D / 32;        // depth steps of K Q^T
   static constexpr int MT = D / 16;        // 16-wide head-dim tiles of O^T
   static constexpr int KP = BN / 32;       // 32-key pairs per tile
@@ -39,7 +39,8 @@ struct FwdCfg {
   static constexpr int BUF = 2 * TSZ;      // K (row tile), V (column tile)
   static constexpr int NS = kFwdStages;    // LDS ring depth
 };
-static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * 32, "forward tile shape");
+static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * kFwdWaveRows && kFwdWaveRows % 16 == 0,
+              "forward tile shape");
 
 // Index of the item whose unit range holds `rank` (unit_begin ascending).
 __device__ __forceinline__ int find_item(const int32_t *items, int n, int rank) {
@@ -66,7 +67,7 @@ __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x4 &v) {
 }
 
 template <int D, typename InT, typename OutT>
-__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(16))) __bf16 lds[NS * C::BUF];
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(FwdArgs a) {
   const InT *__restrict__ vg = static_cast<const InT *>(a.v);
 
   // This wavefront's query rows [rw0, rw_end).
-  const int rw0 = r0 + 32 * wave;
-  const int rw_end = min(rw0 + 32, r1);
+  const int rw0 = r0 + kFwdWaveRows * wave;
+  const int rw_end = min(rw0 + kFwdWaveRows, r1);
   const bool has_rows = rw0 < rw_end;
   const int rw_max = rw_end - 1;
 

@@ -15,10 +15,12 @@ namespace segattn {
 //   [6] aux0  [7] aux1  (per-kernel meaning, see below)
 constexpr int kItemWords = 8;
 
-// Forward tile shape: kFwdWaves wavefronts x 32 query rows per workgroup,
-// 64 keys per K/V tile staged through LDS in a ring of kFwdStages tiles.
+// Forward tile shape: kFwdWaves wavefronts x kFwdWaveRows query rows per
+// workgroup, 64 keys per K/V tile staged through LDS in a ring of
+// kFwdStages tiles.
 constexpr int kFwdWaves = 8;
-constexpr int kFwdBM = 32 * kFwdWaves;
+constexpr int kFwdWaveRows = 32;
+constexpr int kFwdBM = kFwdWaveRows * kFwdWaves;
 constexpr int kFwdBN = 64;
 constexpr int kFwdStages = 4;
 
