@@ -69,7 +69,14 @@ __device__ __forceinline__ void put4<__bf16>(__bf16 *p, const f32x4 &v, int) {
   *reinterpret_cast<u32x2 *>(p) = (u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-__device__ __forceinline__ int find_unit(const int32_t *tab, int words, int field, int n, int rank) {
+// The plan tables (items, key groups, query groups) are read through the
+// constant address space: they are not written while the kernel runs, and
+// wave-uniform reads of them become scalar loads.  Vector loads would be
+// waited for with vmcnt(0), which also waits for every tile copy in flight.
+typedef const __attribute__((address_space(4))) int32_t *ctab;
+__device__ __forceinline__ ctab as_ctab(const int32_t *p) { return (ctab)p; }
+
+__device__ __forceinline__ int find_unit(ctab tab, int words, int field, int n, int rank) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -91,16 +98,16 @@ struct KvStep {
 
 // Next step at or below item i: the first item (walking down) of sequence
 // seq_off whose keys meet [kt0, kt1) and whose queries reach past kt0.
-__device__ __forceinline__ KvStep kv_first_from(const int32_t *items, int i, int seq_off, int kt0, int kt1) {
+__device__ __forceinline__ KvStep kv_first_from(ctab items, int i, int seq_off, int kt0, int kt1) {
   for (; i >= 0; --i) {
-    const int32_t *it = items + i * kItemWords;
+    const ctab it = items + i * kItemWords;
     if (it[0] == seq_off && it[3] < kt1 && it[4] > kt0 && it[2] > kt0) return KvStep{i, 0, max(it[1], kt0)};
   }
   return KvStep{-1, 0, 0};
 }
 
-__device__ __forceinline__ KvStep kv_advance(const int32_t *items, KvStep s, int G, int seq_off, int kt0, int kt1) {
-  const int32_t *it = items + s.item * kItemWords;
+__device__ __forceinline__ KvStep kv_advance(ctab items, KvStep s, int G, int seq_off, int kt0, int kt1) {
+  const ctab it = items + s.item * kItemWords;
   s.qt0 += kBwdKvBM;
   if (s.qt0 < it[2]) return s;
   if (++s.hh < G) {
@@ -112,14 +119,17 @@ __device__ __forceinline__ KvStep kv_advance(const int32_t *items, KvStep s, int
 
 // LDS of the backward kernel.  Each role carves the same block its own way:
 //   dK/dV role: a ring of kBwdKvStages (Q, dO) 64-row tile pairs, their row
-//     statistics, and as many P hand-over buffers;
+//     statistics, and the P hand-over buffers (kKvPBufs);
 //   dQ role:    a ring of kBwdQStages (K, V) 64-key tile pairs.
 template <int D>
 struct BwdLds {
   static constexpr int kTile = kTileRows * D;                     // bf16 elements of one tile
   static constexpr int kKvRing = kBwdKvStages * 2 * kTile * 2;    // bytes
   static constexpr int kKvStat = kBwdKvStages * 2 * kBwdKvBM * 4;
-  static constexpr int kKvP = kBwdKvStages * 4 * 2 * 2 * 64 * 16;  // [stage][group][half][key block][lane] x 16 B
+  // P of step i is written in step i and read in step i+1: two buffers (by
+  // step parity) suffice when the ring length is even.
+  static constexpr int kKvPBufs = kBwdKvStages % 2 == 0 ? 2 : kBwdKvStages;
+  static constexpr int kKvP = kKvPBufs * 4 * 2 * 2 * 64 * 16;  // [buffer][group][half][key block][lane] x 16 B
   static constexpr int kKv = kKvRing + kKvStat + kKvP;
   static constexpr int kQ = kBwdQStages * 2 * kTile * 2;
   static constexpr int kBytes = kKv > kQ ? kKv : kQ;
@@ -138,7 +148,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   __bf16 *lds = reinterpret_cast<__bf16 *>(smem);
   float(*stat)[2][BQ] = reinterpret_cast<float(*)[2][BQ]>(smem + L::kKvRing);
   // P of a tile, handed from each group's dV wavefront to its dK wavefront:
-  // [stage][group][32-row half][16-key block][lane] x 8 bf16 values (the very
+  // [buffer][group][32-row half][16-key block][lane] x 8 bf16 values (the very
   // operand of dV += P^T dO; bf16 keeps fp32's exponent range, which matters
   // at a million keys where P ~ 1e-6 would be subnormal in fp16).
   uint32_t(*pshare)[NG][2][2][64][4] = reinterpret_cast<uint32_t(*)[NG][2][2][64][4]>(smem + L::kKvRing + L::kKvStat);
@@ -155,13 +165,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
 
   int rank, g;
   map_xcd(x, a.hkv, a.n_kv_units, rank, g);
-  const int32_t *kv = a.kvg + find_unit(a.kvg, 4, 3, a.n_kvg, rank) * 4;
+  const ctab kv = as_ctab(a.kvg) + find_unit(as_ctab(a.kvg), 4, 3, a.n_kvg, rank) * 4;
   const int seq_off = kv[0], kb = kv[1], ke = kv[2];
   const int kt0 = kb + (rank - kv[3]) * kBwdKvBN;
   const int kt1 = min(ke, kt0 + kBwdKvBN);
   const int G = a.hq / a.hkv;
   const int64_t T = a.tokens;
-  const int32_t *__restrict__ items = a.items;
+  const ctab items = as_ctab(a.items);
   const float *__restrict__ lse = a.lse;
   const float *__restrict__ delta = a.delta;
   const int hq = a.hq, hkv = a.hkv;
@@ -204,13 +214,17 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
 
   const int64_t qstride = (int64_t)hq * D;
+  // The fragment loads above complete here, before the first tile copy: the
+  // compiler then knows they are done, instead of waiting for vmcnt(0) (the
+  // tile copies in flight included) before their first use in every step.
+  wait_vm<0>();
   using Loader = TileLoader<D, InT, W>;
   Loader lqd;  // Q and dO tiles: same rows and stride
   lqd.init(wave, lane, qstride);
   // Stage s of the ring: the Q and dO tiles of step `st`, and (wavefront 0)
   // the tile's natural-log LSE and D rows.
   auto stage = [&](const KvStep &st, int s) __attribute__((always_inline)) {
-    const int32_t *it = items + st.item * kItemWords;
+    const ctab it = items + st.item * kItemWords;
     const int h = g * G + st.hh;
     const int nvalid = min(BQ, it[2] - st.qt0);
     const int64_t row0 = (int64_t)seq_off + st.qt0;
@@ -226,17 +240,25 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   const float c2 = a.scale_log2;
   // Three walkers over the same step sequence: `ld` (staged), `cp` (the dV
   // wavefronts' step) and `pk` (the dK wavefronts' step, one behind).
-  // Iteration i: stage i is published; stage i+1 is copied into the slot
+  // Iteration i: stage i is published; stage i+AHEAD is copied into the slot
   // that step i-2 used (finished by both roles); the dV wavefronts work on
-  // step i in slot i % NS and hand P over in buffer i % NS; the dK
+  // step i in slot i % NS and hand P over in buffer i % NP; the dK
   // wavefronts work on step i-1 in slot (i-1) % NS with its P.
+  constexpr int AHEAD = NS - 2;         // stages copied ahead of the dV step
+  constexpr int NP = L::kKvPBufs;       // P hand-over buffers
+  constexpr int LW = 2 * Loader::kInstr;  // copies per stage (wavefront 0: + 2 rows of statistics)
+  static_assert(AHEAD >= 1 && (NP == 2 || NP == NS), "dK/dV ring");
   KvStep cp = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
   KvStep pk{-1, 0, 0};
   KvStep ld = cp;
-  if (ld.item >= 0) {
-    stage(ld, 0);
-    ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
-  }
+  int issued = 0, done = 0;  // stages copied / steps of the dV wavefronts started
+#pragma unroll
+  for (int s = 0; s < AHEAD; ++s)
+    if (ld.item >= 0) {
+      stage(ld, s);
+      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ++issued;
+    }
   // Rows: half qp, sub-block ab of a 32-row half reads query rows
   // 32qp + 8*(m/4) + 4*ab + m%4, so a lane's 8 values of a half are the rows
   // 32qp + 8*lg + 0..7 for its key 16nk + l16 -- the A operand layout of the
@@ -245,15 +267,20 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
     constexpr int bv = decltype(slot)::value;  // dV role: step i
     constexpr int bk = (bv + NS - 1) % NS;     // dK role: step i-1
-    wait_vm<0>();
-    __syncthreads();  // stage i visible; P of step i-1 visible; slot (i+1) % NS free
+    // stage i landed; the stages copied after it may stay in flight
+    if (wave == 0)
+      wait_stages<LW + 2, 3>(issued - done - 1);
+    else
+      wait_stages<LW, 3>(issued - done - 1);
+    ring_barrier();  // stage i visible; P of step i-1 visible; slot (i+AHEAD) % NS free
     if (ld.item >= 0) {
-      stage(ld, (bv + 1) % NS);
+      stage(ld, (bv + AHEAD) % NS);
       ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ++issued;
     }
     const KvStep st = dk_role ? pk : cp;
     if (st.item >= 0) {
-      const int32_t *it = items + st.item * kItemWords;
+      const ctab it = items + st.item * kItemWords;
       const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
       const int qt0 = st.qt0;
       const int qt1 = min(qt0 + BQ, q_hi);
@@ -315,7 +342,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
                     pv[ab][i] = p;
                   }
                 opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
-                *reinterpret_cast<bf16x8 *>(pshare[bv][kgrp][qp][nk][lane]) = opa[qp][nk];
+                *reinterpret_cast<bf16x8 *>(pshare[bv % NP][kgrp][qp][nk][lane]) = opa[qp][nk];
               }
             }
           };
@@ -331,7 +358,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
             const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg + 4]);
 #pragma unroll
             for (int nk = 0; nk < 2; ++nk) {
-              const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk][kgrp][qp][nk][lane]);
+              const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk % NP][kgrp][qp][nk][lane]);
               f32x4 ds[2];
 #pragma unroll
               for (int ab = 0; ab < 2; ++ab)
@@ -368,7 +395,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
       }
     }
     pk = cp;
-    if (cp.item >= 0) cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
+    if (cp.item >= 0) {
+      cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
+      ++done;
+    }
     return pk.item >= 0;
   };
   if (cp.item >= 0)
@@ -400,15 +430,15 @@ struct QStep {
 
 // Next step at or below item i of a query group (items first..): the first
 // item (walking down) with a key inside [k_lo, min(k_hi, r1)).
-__device__ __forceinline__ QStep q_first_from(const int32_t *items, int i, int first, int r1) {
+__device__ __forceinline__ QStep q_first_from(ctab items, int i, int first, int r1) {
   for (; i >= first; --i) {
-    const int32_t *it = items + i * kItemWords;
+    const ctab it = items + i * kItemWords;
     if (min(it[4], r1) > it[3]) return QStep{i, it[3]};
   }
   return QStep{-1, 0};
 }
 
-__device__ __forceinline__ QStep q_advance(const int32_t *items, QStep s, int first, int r1) {
+__device__ __forceinline__ QStep q_advance(ctab items, QStep s, int first, int r1) {
   s.kv0 += kBwdQBN;
   if (s.kv0 < min(items[s.item * kItemWords + 4], r1)) return s;
   return q_first_from(items, s.item - 1, first, r1);
@@ -429,13 +459,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
 
   int rank, h;
   map_xcd(x, a.hq, a.n_q_units, rank, h);
-  const int32_t *__restrict__ items = a.items;
+  const ctab items = as_ctab(a.items);
   const float *__restrict__ lse = a.lse;
   const float *__restrict__ delta = a.delta;
   const int hq = a.hq, hkv = a.hkv;
-  const int32_t *grp = a.qg + find_unit(a.qg, 4, 2, a.n_qg, rank) * 4;
+  const ctab grp = as_ctab(a.qg) + find_unit(as_ctab(a.qg), 4, 2, a.n_qg, rank) * 4;
   const int first = grp[0], count = grp[1];
-  const int32_t *it0 = items + first * kItemWords;
+  const ctab it0 = items + first * kItemWords;
   const int seq_off = it0[0], q_lo = it0[1], q_hi = it0[2];
   const int r1 = q_hi - (rank - grp[2]) * kBwdQBM;
   const int r0 = max(q_lo, r1 - kBwdQBM);
@@ -487,6 +517,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
 
   const int64_t kstride = (int64_t)hkv * D;
+  // The fragment loads above complete here, before the first tile copy: the
+  // compiler then knows they are done, instead of waiting for vmcnt(0) (the
+  // tile copies in flight included) before their first use in every step.
+  wait_vm<0>();
   using Loader = TileLoader<D, InT, kBwdQWaves>;
   Loader lkv;  // K and V tiles: same rows and stride
   lkv.init(wave, lane, kstride);
@@ -513,7 +547,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(slot)::value;
     wait_stages<2 * Loader::kInstr, NS>(issued - done - 1);
-    __syncthreads();  // stage `buf` visible; the slot staged next is free
+    ring_barrier();  // stage `buf` visible; the slot staged next is free
     if (ld.item >= 0) {
       stage(ld, (buf + NS - 1) % NS);
       ld = q_advance(items, ld, first, r1);

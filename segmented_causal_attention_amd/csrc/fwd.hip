@@ -136,6 +136,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
 
   // K and V tiles of 64 keys starting at key kvs, staged into ring slot `slot`.
   const int64_t kvstride = (int64_t)hkv * D;
+  // The fragment loads above complete here, before the first tile copy: the
+  // compiler then knows they are done, instead of waiting for vmcnt(0) (the
+  // tile copies in flight included) before their first use in every step.
+  wait_vm<0>();
   using Loader = TileLoader<D, InT, C::W>;
   Loader lkv;
   lkv.init(wave, lane, kvstride);
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(slot)::value;
     wait_stages<2 * Loader::kInstr, NS>(issued - j - 1);
-    __syncthreads();  // tile `buf` visible; the slot staged next is free
+    ring_barrier();  // tile `buf` visible; the slot staged next is free
     if (issued < ntiles) {
       stage(kb + issued * C::BN, (buf + NS - 1) % NS);
       ++issued;

@@ -20,6 +20,17 @@
 // with one global_load_lds_dwordx4 (global memory straight to LDS, no
 // registers).
 //
+// Those copies are issued from inline assembly (dma_to_lds) and the rings are
+// published with ring_barrier() instead of __syncthreads().  With the
+// compiler builtin, the compiler cannot tell which ring slot a copy writes,
+// so it waits for every copy in flight (vmcnt 0) before the first LDS read
+// that follows one and, through __syncthreads()'s release fence, before every
+// barrier -- including the copies of the next 2-3 tiles, which defeats the
+// ring.  The kernels count their own copies instead (wait_vm / wait_stages
+// before each ring_barrier).  Vector-memory loads complete in issue order, so
+// the compiler's own vmcnt waits for its loads stay correct with these extra
+// copies outstanding (they only become stricter).
+//
 // The per-lane byte offsets of every read are loop invariant; kernels compute
 // them once (row_read_off / col_read_off) and add compile-time immediates for
 // the pair, half and buffer indices (the swizzles ignore row bits 2 and 5).
@@ -33,6 +44,30 @@ namespace segattn {
 namespace dev {
 
 constexpr int kTileRows = 64;
+
+// Direct copy global -> LDS of BYTES (4 or 16) per lane: lane i's bytes at
+// src (its own address) land at lds_dst + BYTES * i.  M0 holds the
+// wave-uniform LDS destination; no instruction the compiler generates in
+// these kernels keeps a value in M0, so clobbering it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void *src, const void *lds_dst) {
+  static_assert(BYTES == 4 || BYTES == 16, "copy width");
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds_dst);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier of the LDS rings: this wavefront's LDS reads and writes
+// are complete (lgkmcnt 0), then s_barrier.  Its direct copies must already
+// be covered by a vmcnt wait (wait_vm / wait_stages).  The asm statement is
+// also a compiler barrier for memory accesses.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 constexpr int kRowTile = 0;  // read with 16-byte row reads
 constexpr int kColTile = 1;  // read with 8-byte transposing reads
@@ -132,9 +167,7 @@ struct TileLoader<D, __bf16, W> {
       int off = off_[KIND][t];
       if (nvalid < kTileRows && row_[t] >= nvalid)  // partial tile: repeat the last valid row
         off += (nvalid - 1 - row_[t]) * stride_;
-      __builtin_amdgcn_global_load_lds((const void *)(src + off),
-                                       (__attribute__((address_space(3))) void *)(tile + (wave_ * NI + t) * RPI * D),
-                                       16, 0, 0);
+      dma_to_lds<16>(src + off, tile + (wave_ * NI + t) * RPI * D);
     }
   }
 };
@@ -170,8 +203,7 @@ struct TileLoader<D, float, W> {
 // 64 consecutive floats (one per lane; lanes >= nvalid repeat element
 // nvalid-1) copied straight into LDS by one wavefront.
 __device__ __forceinline__ void stage_row_floats(float *dst, const float *src, int nvalid, int lane) {
-  __builtin_amdgcn_global_load_lds((const void *)(src + min(lane, nvalid - 1)),
-                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+  dma_to_lds<4>(src + min(lane, nvalid - 1), dst);
 }
 
 // Waits until at most N of this wavefront's vector memory operations are
