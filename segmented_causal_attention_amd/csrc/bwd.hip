@@ -76,6 +76,16 @@ __device__ __forceinline__ void put4<__bf16>(__bf16 *p, const f32x4 &v, int) {
 typedef const __attribute__((address_space(4))) int32_t *ctab;
 __device__ __forceinline__ ctab as_ctab(const int32_t *p) { return (ctab)p; }
 
+// One row of the item table (kItemWords words) in a single scalar load.  The
+// walkers below keep the ranges of their current item in registers and read
+// the table only when they move to another item, so a step does not wait
+// for table loads.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+static_assert(kItemWords == 8, "item rows are loaded as 8 words");
+__device__ __forceinline__ i32x8 item_row(ctab items, int i) {
+  return *(const __attribute__((address_space(4))) i32x8 *)(items + i * kItemWords);
+}
+
 __device__ __forceinline__ int find_unit(ctab tab, int words, int field, int n, int rank) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
@@ -94,24 +104,25 @@ struct KvStep {
   int item;  // < 0: done
   int hh;    // query head within the group
   int qt0;   // first query row of the tile (sequence-local)
+  int q_lo, q_hi, k_lo, k_hi;  // the item's query and key ranges
 };
 
 // Next step at or below item i: the first item (walking down) of sequence
 // seq_off whose keys meet [kt0, kt1) and whose queries reach past kt0.
 __device__ __forceinline__ KvStep kv_first_from(ctab items, int i, int seq_off, int kt0, int kt1) {
   for (; i >= 0; --i) {
-    const ctab it = items + i * kItemWords;
-    if (it[0] == seq_off && it[3] < kt1 && it[4] > kt0 && it[2] > kt0) return KvStep{i, 0, max(it[1], kt0)};
+    const i32x8 r = item_row(items, i);
+    if (r[0] == seq_off && r[3] < kt1 && r[4] > kt0 && r[2] > kt0)
+      return KvStep{i, 0, max(r[1], kt0), r[1], r[2], r[3], r[4]};
   }
-  return KvStep{-1, 0, 0};
+  return KvStep{-1, 0, 0, 0, 0, 0, 0};
 }
 
 __device__ __forceinline__ KvStep kv_advance(ctab items, KvStep s, int G, int seq_off, int kt0, int kt1) {
-  const ctab it = items + s.item * kItemWords;
   s.qt0 += kBwdKvBM;
-  if (s.qt0 < it[2]) return s;
+  if (s.qt0 < s.q_hi) return s;
   if (++s.hh < G) {
-    s.qt0 = max(it[1], kt0);
+    s.qt0 = max(s.q_lo, kt0);
     return s;
   }
   return kv_first_from(items, s.item - 1, seq_off, kt0, kt1);
@@ -224,9 +235,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   // Stage s of the ring: the Q and dO tiles of step `st`, and (wavefront 0)
   // the tile's natural-log LSE and D rows.
   auto stage = [&](const KvStep &st, int s) __attribute__((always_inline)) {
-    const ctab it = items + st.item * kItemWords;
     const int h = g * G + st.hh;
-    const int nvalid = min(BQ, it[2] - st.qt0);
+    const int nvalid = min(BQ, st.q_hi - st.qt0);
     const int64_t row0 = (int64_t)seq_off + st.qt0;
     __bf16 *b = lds + s * BUF;
     lqd.template stage<kColTile>(b, qg + (row0 * hq + h) * D, nvalid);
@@ -249,7 +259,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   constexpr int LW = 2 * Loader::kInstr;  // copies per stage (wavefront 0: + 2 rows of statistics)
   static_assert(AHEAD >= 1 && (NP == 2 || NP == NS), "dK/dV ring");
   KvStep cp = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
-  KvStep pk{-1, 0, 0};
+  KvStep pk{-1, 0, 0, 0, 0, 0, 0};
   KvStep ld = cp;
   int issued = 0, done = 0;  // stages copied / steps of the dV wavefronts started
 #pragma unroll
@@ -280,8 +290,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
     }
     const KvStep st = dk_role ? pk : cp;
     if (st.item >= 0) {
-      const ctab it = items + st.item * kItemWords;
-      const int k_lo = it[3], k_hi = it[4], q_hi = it[2];
+      const int k_lo = st.k_lo, k_hi = st.k_hi, q_hi = st.q_hi;
       const int qt0 = st.qt0;
       const int qt1 = min(qt0 + BQ, q_hi);
       if (has_keys && kw0 < qt1) {
@@ -424,23 +433,26 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
 // ====================================================================== dQ
 
 struct QStep {
-  int item;  // < 0: done
-  int kv0;
+  int item;   // < 0: done
+  int kv0;    // first key of the tile
+  int k_end;  // min(k_hi, r1): end of the item's keys that this tile's rows can see
+  int k_hi;   // the item's key range end
 };
 
 // Next step at or below item i of a query group (items first..): the first
 // item (walking down) with a key inside [k_lo, min(k_hi, r1)).
 __device__ __forceinline__ QStep q_first_from(ctab items, int i, int first, int r1) {
   for (; i >= first; --i) {
-    const ctab it = items + i * kItemWords;
-    if (min(it[4], r1) > it[3]) return QStep{i, it[3]};
+    const i32x8 r = item_row(items, i);
+    const int e = min(r[4], r1);
+    if (e > r[3]) return QStep{i, r[3], e, r[4]};
   }
-  return QStep{-1, 0};
+  return QStep{-1, 0, 0, 0};
 }
 
 __device__ __forceinline__ QStep q_advance(ctab items, QStep s, int first, int r1) {
   s.kv0 += kBwdQBN;
-  if (s.kv0 < min(items[s.item * kItemWords + 4], r1)) return s;
+  if (s.kv0 < s.k_end) return s;
   return q_first_from(items, s.item - 1, first, r1);
 }
 
@@ -504,7 +516,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) dq[nq][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto item_end = [&](int i) __attribute__((always_inline)) { return min(items[i * kItemWords + 4], r1); };
 
   // Loop-invariant LDS byte offsets of this lane's reads.
   int rkoff[C::KS], rvoff[C::KS], coff[C::NT];
@@ -525,7 +536,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   Loader lkv;  // K and V tiles: same rows and stride
   lkv.init(wave, lane, kstride);
   auto stage = [&](const QStep &st, int s) __attribute__((always_inline)) {
-    const int nvalid = min(BN, item_end(st.item) - st.kv0);
+    const int nvalid = min(BN, st.k_end - st.kv0);
     const int64_t off = (((int64_t)seq_off + st.kv0) * hkv + g) * D;
     __bf16 *b = lds + s * BUF;
     lkv.template stage<kColTile>(b, kg + off, nvalid);
@@ -554,7 +565,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
       ++issued;
     }
     const int kv0 = cp.kv0;
-    const int k_hi = items[cp.item * kItemWords + 4];
+    const int k_hi = cp.k_hi;
     if (has_rows && kv0 <= rw_end - 1) {
       const __bf16 *Ks = lds + buf * BUF, *Vs = Ks + C::TSZ;
       const bool need_mask = (kv0 + BN - 1 > rw0) || (kv0 + BN > k_hi);
