@@ -169,8 +169,8 @@ int segattn_merge(int64_t rows, int32_t h, int32_t d, int64_t lse_stride,
 int segattn_bwd_workspace(const segattn_shape *shape, const segattn_item *items, int32_t n_items,
                           size_t *bytes);
 
-/* D_q = <dO_q, O_q> for every query row of the items, into the workspace
- * (float [hq][tokens] at its start).  Lets the caller time or schedule the
+/* D_q = <dO_q, O_q> for every query row of the items, stored NEGATED (-D_q)
+ * into the workspace (float [hq][tokens] at its start).  Lets the caller time or schedule the
  * reduction apart from the main backward kernel; segattn_bwd then takes
  * SEGATTN_D_READY.  Arguments as in segattn_bwd. */
 int segattn_bwd_preprocess(const segattn_shape *shape, const void *o, int32_t o_dtype, const void *d_o,

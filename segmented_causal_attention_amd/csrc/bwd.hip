@@ -1,7 +1,8 @@
 // Backward kernels for gfx950 (CDNA4), bf16 MFMA, fp32 accumulation.
 //
 // Gradients of f = sum(dO * O) for the items' attention, given the forward's
-// final LSE and D = <dO, O> (computed beforehand):
+// final LSE and D = <dO, O> (computed beforehand and stored negated: the dP
+// products start their accumulators from -D and so yield dP - D directly):
 //   P = exp(scale <Q, K> - LSE),  dV += P^T dO,  dP = dO V^T,
 //   dS = P (dP - D),  dQ += scale dS K,  dK += scale dS^T Q.
 // InfiniPipe section II-A: a slice's backward runs after those of the slices
@@ -105,28 +106,49 @@ struct KvStep {
   int hh;    // query head within the group
   int qt0;   // first query row of the tile (sequence-local)
   int q_lo, q_hi, k_lo, k_hi;  // the item's query and key ranges
+  int64_t qoff;  // element offset of the tile's first Q / dO row: ((seq_off + qt0) hq + h) d
+  int64_t soff;  // offset of its first LSE / D entry: h T + seq_off + qt0
 };
 
-// Next step at or below item i: the first item (walking down) of sequence
-// seq_off whose keys meet [kt0, kt1) and whose queries reach past kt0.
-__device__ __forceinline__ KvStep kv_first_from(ctab items, int i, int seq_off, int kt0, int kt1) {
-  for (; i >= 0; --i) {
-    const i32x8 r = item_row(items, i);
-    if (r[0] == seq_off && r[3] < kt1 && r[4] > kt0 && r[2] > kt0)
-      return KvStep{i, 0, max(r[1], kt0), r[1], r[2], r[3], r[4]};
+// What the dK/dV walker needs to know about its workgroup.
+struct KvWalk {
+  ctab items;
+  int G, seq_off, kt0, kt1, g, hq, d;
+  int64_t T;
+  __device__ __forceinline__ void offsets(KvStep &s) const {
+    const int64_t h = (int64_t)g * G + s.hh, row = (int64_t)seq_off + s.qt0;
+    s.qoff = (row * hq + h) * d;
+    s.soff = h * T + row;
   }
-  return KvStep{-1, 0, 0, 0, 0, 0, 0};
-}
-
-__device__ __forceinline__ KvStep kv_advance(ctab items, KvStep s, int G, int seq_off, int kt0, int kt1) {
-  s.qt0 += kBwdKvBM;
-  if (s.qt0 < s.q_hi) return s;
-  if (++s.hh < G) {
-    s.qt0 = max(s.q_lo, kt0);
-    return s;
+  // Next step at or below item i: the first item (walking down) of sequence
+  // seq_off whose keys meet [kt0, kt1) and whose queries reach past kt0.
+  __device__ __forceinline__ KvStep first_from(int i) const {
+    for (; i >= 0; --i) {
+      const i32x8 r = item_row(items, i);
+      if (r[0] == seq_off && r[3] < kt1 && r[4] > kt0 && r[2] > kt0) {
+        KvStep s{i, 0, max(r[1], kt0), r[1], r[2], r[3], r[4], 0, 0};
+        offsets(s);
+        return s;
+      }
+    }
+    return KvStep{-1, 0, 0, 0, 0, 0, 0, 0, 0};
   }
-  return kv_first_from(items, s.item - 1, seq_off, kt0, kt1);
-}
+  // The next 64-row tile: within a run of tiles the offsets just move on.
+  __device__ __forceinline__ KvStep advance(KvStep s) const {
+    s.qt0 += kBwdKvBM;
+    if (s.qt0 < s.q_hi) {
+      s.qoff += (int64_t)kBwdKvBM * hq * d;
+      s.soff += kBwdKvBM;
+      return s;
+    }
+    if (++s.hh < G) {
+      s.qt0 = max(s.q_lo, kt0);
+      offsets(s);
+      return s;
+    }
+    return first_from(s.item - 1);
+  }
+};
 
 // LDS of the backward kernel.  Each role carves the same block its own way:
 //   dK/dV role: a ring of kBwdKvStages (Q, dO) 64-row tile pairs, their row
@@ -157,6 +179,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   constexpr int BUF = 2 * C::TSZ;  // Q, dO (column layout, read both ways)
   static_assert(NG == 4 && BUF == 2 * L::kTile, "backward LDS layout");
   __bf16 *lds = reinterpret_cast<__bf16 *>(smem);
+  const uint32_t lds0 = lds_addr(smem);  // LDS byte address of the block
   float(*stat)[2][BQ] = reinterpret_cast<float(*)[2][BQ]>(smem + L::kKvRing);
   // P of a tile, handed from each group's dV wavefront to its dK wavefront:
   // [buffer][group][32-row half][16-key block][lane] x 8 bf16 values (the very
@@ -235,15 +258,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   // Stage s of the ring: the Q and dO tiles of step `st`, and (wavefront 0)
   // the tile's natural-log LSE and D rows.
   auto stage = [&](const KvStep &st, int s) __attribute__((always_inline)) {
-    const int h = g * G + st.hh;
     const int nvalid = min(BQ, st.q_hi - st.qt0);
-    const int64_t row0 = (int64_t)seq_off + st.qt0;
     __bf16 *b = lds + s * BUF;
-    lqd.template stage<kColTile>(b, qg + (row0 * hq + h) * D, nvalid);
-    lqd.template stage<kColTile>(b + C::TSZ, dg + (row0 * hq + h) * D, nvalid);
+    const uint32_t ba = lds0 + s * BUF * 2;
+    lqd.template stage<kColTile>(b, ba, qg + st.qoff, nvalid);
+    lqd.template stage<kColTile>(b + C::TSZ, ba + C::TSZ * 2, dg + st.qoff, nvalid);
     if (wave == 0) {
-      stage_row_floats(&stat[s][0][0], lse + (int64_t)h * T + row0, nvalid, lane);
-      stage_row_floats(&stat[s][1][0], delta + (int64_t)h * T + row0, nvalid, lane);
+      const uint32_t sa = lds0 + L::kKvRing + s * 2 * BQ * 4;  // stat[s][0], stat[s][1]
+      stage_row_floats(sa, lse + st.soff, nvalid, lane);
+      stage_row_floats(sa + BQ * 4, delta + st.soff, nvalid, lane);
     }
   };
 
@@ -258,15 +281,16 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   constexpr int NP = L::kKvPBufs;       // P hand-over buffers
   constexpr int LW = 2 * Loader::kInstr;  // copies per stage (wavefront 0: + 2 rows of statistics)
   static_assert(AHEAD >= 1 && (NP == 2 || NP == NS), "dK/dV ring");
-  KvStep cp = kv_first_from(items, a.n_items - 1, seq_off, kt0, kt1);
-  KvStep pk{-1, 0, 0, 0, 0, 0, 0};
+  const KvWalk walk{items, G, seq_off, kt0, kt1, g, hq, D, T};
+  KvStep cp = walk.first_from(a.n_items - 1);
+  KvStep pk{-1, 0, 0, 0, 0, 0, 0, 0, 0};
   KvStep ld = cp;
   int issued = 0, done = 0;  // stages copied / steps of the dV wavefronts started
 #pragma unroll
   for (int s = 0; s < AHEAD; ++s)
     if (ld.item >= 0) {
       stage(ld, s);
-      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ld = walk.advance(ld);
       ++issued;
     }
   // Rows: half qp, sub-block ab of a 32-row half reads query rows
@@ -278,14 +302,16 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
     constexpr int bv = decltype(slot)::value;  // dV role: step i
     constexpr int bk = (bv + NS - 1) % NS;     // dK role: step i-1
     // stage i landed; the stages copied after it may stay in flight
-    if (wave == 0)
+    if constexpr (AHEAD == 1)
+      wait_vm<0>();  // only stage i was in flight
+    else if (wave == 0)
       wait_stages<LW + 2, 3>(issued - done - 1);
     else
       wait_stages<LW, 3>(issued - done - 1);
     ring_barrier();  // stage i visible; P of step i-1 visible; slot (i+AHEAD) % NS free
     if (ld.item >= 0) {
       stage(ld, (bv + AHEAD) % NS);
-      ld = kv_advance(items, ld, G, seq_off, kt0, kt1);
+      ld = walk.advance(ld);
       ++issued;
     }
     const KvStep st = dk_role ? pk : cp;
@@ -298,31 +324,44 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
         const __bf16 *Qs = lds + b * BUF, *dOs = Qs + C::TSZ;
         const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows: S = Q K^T or dP = dO V^T
         bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
-        f32x4 xs[2][2][2];                      // [qp][ab][nk]: S or dP
+        f32x4 xs[2][2][2];                      // [qp][ab][nk]: S or dP - D
+        // The contraction over the head dim.  The dV role starts from zero
+        // (S); the dK role from -D of the lane's rows (dP - D).  One copy
+        // per role, so neither carries the other's start values.
+        auto contract = [&](auto dkc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qp = 0; qp < 2; ++qp)
+          for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
-          for (int ab = 0; ab < 2; ++ab)
+            for (int ab = 0; ab < 2; ++ab) {
+              f32x4 x0 = (f32x4){0.f, 0.f, 0.f, 0.f};
+              if constexpr (decltype(dkc)::value)  // -D of rows 32qp + 8lg + 4ab + 0..3
+                x0 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg + 4 * ab]);
 #pragma unroll
-            for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
-        pipelined<2 * C::KS>(
-            [&](auto ic) __attribute__((always_inline)) {
-              constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
-              struct {
-                bf16x8 f[2];
-              } xa;
+              for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = x0;
+            }
+          // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
+          pipelined<2 * C::KS>(
+              [&](auto ic) __attribute__((always_inline)) {
+                constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+                struct {
+                  bf16x8 f[2];
+                } xa;
 #pragma unroll
-              for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
-              return xa;
-            },
-            [&](auto ic, const auto &xa) __attribute__((always_inline)) {
-              constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+                for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+                return xa;
+              },
+              [&](auto ic, const auto &xa) __attribute__((always_inline)) {
+                constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
 #pragma unroll
-              for (int ab = 0; ab < 2; ++ab)
+                for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-                for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], xs[qp][ab][nk]);
-            });
+                  for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], xs[qp][ab][nk]);
+              });
+        };
+        if (dk_role)
+          contract(std::true_type{});
+        else
+          contract(std::false_type{});
         if (!dk_role) {
           // P = exp(S - LSE), masked on boundary tiles.  Rows past q_hi of a
           // partial tile repeat the last row in LDS and must drop out too.
@@ -363,8 +402,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
           // dS = P (dP - D) with the P the dV wavefront left one iteration ago
 #pragma unroll
           for (int qp = 0; qp < 2; ++qp) {
-            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg]);
-            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg + 4]);
 #pragma unroll
             for (int nk = 0; nk < 2; ++nk) {
               const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk % NP][kgrp][qp][nk][lane]);
@@ -375,7 +412,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
                 for (int i = 0; i < 4; ++i) {
                   const uint32_t w = ph[2 * ab + (i >> 1)];
                   const float p = (i & 1) ? bf16_hi(w) : bf16_lo(w);
-                  ds[ab][i] = p * (xs[qp][ab][nk][i] - (ab ? d1[i] : d0[i]));
+                  ds[ab][i] = p * xs[qp][ab][nk][i];
                 }
               opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
             }
@@ -405,7 +442,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
     }
     pk = cp;
     if (cp.item >= 0) {
-      cp = kv_advance(items, cp, G, seq_off, kt0, kt1);
+      cp = walk.advance(cp);
       ++done;
     }
     return pk.item >= 0;
@@ -437,24 +474,30 @@ struct QStep {
   int kv0;    // first key of the tile
   int k_end;  // min(k_hi, r1): end of the item's keys that this tile's rows can see
   int k_hi;   // the item's key range end
+  int64_t kvoff;  // element offset of the tile's first K / V row: ((seq_off + kv0) hkv + g) d
 };
 
-// Next step at or below item i of a query group (items first..): the first
-// item (walking down) with a key inside [k_lo, min(k_hi, r1)).
-__device__ __forceinline__ QStep q_first_from(ctab items, int i, int first, int r1) {
-  for (; i >= first; --i) {
-    const i32x8 r = item_row(items, i);
-    const int e = min(r[4], r1);
-    if (e > r[3]) return QStep{i, r[3], e, r[4]};
+// What the dQ walker needs to know about its workgroup.
+struct QWalk {
+  ctab items;
+  int first, r1, seq_off, hkv, g, d;
+  // Next step at or below item i of the query group (items first..): the
+  // first item (walking down) with a key inside [k_lo, min(k_hi, r1)).
+  __device__ __forceinline__ QStep first_from(int i) const {
+    for (; i >= first; --i) {
+      const i32x8 r = item_row(items, i);
+      const int e = min(r[4], r1);
+      if (e > r[3]) return QStep{i, r[3], e, r[4], (((int64_t)seq_off + r[3]) * hkv + g) * d};
+    }
+    return QStep{-1, 0, 0, 0, 0};
   }
-  return QStep{-1, 0, 0, 0};
-}
-
-__device__ __forceinline__ QStep q_advance(ctab items, QStep s, int first, int r1) {
-  s.kv0 += kBwdQBN;
-  if (s.kv0 < s.k_end) return s;
-  return q_first_from(items, s.item - 1, first, r1);
-}
+  __device__ __forceinline__ QStep advance(QStep s) const {
+    s.kv0 += kBwdQBN;
+    s.kvoff += (int64_t)kBwdQBN * hkv * d;
+    if (s.kv0 < s.k_end) return s;
+    return first_from(s.item - 1);
+  }
+};
 
 template <int D, typename InT, typename GT>
 __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
@@ -464,6 +507,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   constexpr int BUF = 2 * C::TSZ;  // K (column layout, read both ways), V (row layout)
   static_assert(NS * BUF * 2 == BwdLds<D>::kQ, "backward LDS layout");
   __bf16 *lds = reinterpret_cast<__bf16 *>(smem);
+  const uint32_t lds0 = lds_addr(smem);  // LDS byte address of the block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -493,7 +537,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   const bool has_rows = rw0 < rw_end;
 
   bf16x8 qf[2][C::KS], dof[2][C::KS];
-  float lse2[2], drow[2];
+  float lse2[2], ndrow[2];  // LSE (base 2) and -D of the lane's two rows
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq) {
     const int row = rw0 + 16 * nq + l16;
@@ -507,7 +551,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
     }
     const float l = ok ? lse[(int64_t)h * T + grow] : kNegInf;
     lse2[nq] = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    drow[nq] = ok ? delta[(int64_t)h * T + grow] : 0.f;
+    ndrow[nq] = ok ? delta[(int64_t)h * T + grow] : 0.f;  // stored as -D
   }
 
   f32x4 dq[2][C::NT];
@@ -537,22 +581,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   lkv.init(wave, lane, kstride);
   auto stage = [&](const QStep &st, int s) __attribute__((always_inline)) {
     const int nvalid = min(BN, st.k_end - st.kv0);
-    const int64_t off = (((int64_t)seq_off + st.kv0) * hkv + g) * D;
     __bf16 *b = lds + s * BUF;
-    lkv.template stage<kColTile>(b, kg + off, nvalid);
-    lkv.template stage<kRowTile>(b + C::TSZ, vg + off, nvalid);
+    const uint32_t ba = lds0 + s * BUF * 2;
+    lkv.template stage<kColTile>(b, ba, kg + st.kvoff, nvalid);
+    lkv.template stage<kRowTile>(b + C::TSZ, ba + C::TSZ * 2, vg + st.kvoff, nvalid);
   };
 
   const float c2 = a.scale_log2;
   // `ld` stages NS-1 steps ahead of `cp`, which is computed.
-  QStep cp = q_first_from(items, first + count - 1, first, r1);
+  const QWalk walk{items, first, r1, seq_off, hkv, g, D};
+  QStep cp = walk.first_from(first + count - 1);
   QStep ld = cp;
   int issued = 0, done = 0;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (ld.item >= 0) {
       stage(ld, s);
-      ld = q_advance(items, ld, first, r1);
+      ld = walk.advance(ld);
       ++issued;
     }
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
@@ -561,7 +606,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
     ring_barrier();  // stage `buf` visible; the slot staged next is free
     if (ld.item >= 0) {
       stage(ld, (buf + NS - 1) % NS);
-      ld = q_advance(items, ld, first, r1);
+      ld = walk.advance(ld);
       ++issued;
     }
     const int kv0 = cp.kv0;
@@ -581,7 +626,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab) {
             s[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            dp[nq][ab] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            // dP^T starts from -D of the lane's query row: it yields dP - D
+            dp[nq][ab] = (f32x4){ndrow[nq], ndrow[nq], ndrow[nq], ndrow[nq]};
           }
         // sub-step ks: the K and V row fragments of depth step ks
         pipelined<C::KS>(
@@ -623,7 +669,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
                   const int key = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
                   if (key > qrow || key >= k_hi) pv = 0.f;
                 }
-                ds[ab][i] = pv * (dp[nq][ab][i] - drow[nq]);
+                ds[ab][i] = pv * dp[nq][ab][i];
               }
             dsb[nq][kp] = pack_bf16x8(ds[0], ds[1]);
           }
@@ -653,7 +699,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
               for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka.f[kp], dsb[nq][kp], dq[nq][nt]);
           });
     }
-    cp = q_advance(items, cp, first, r1);
+    cp = walk.advance(cp);
     ++done;
     return cp.item >= 0;
   };

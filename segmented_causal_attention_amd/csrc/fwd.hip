@@ -71,6 +71,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   using C = FwdCfg<D>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(16))) __bf16 lds[NS * C::BUF];
+  const uint32_t lds0 = lds_addr(lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,9 +146,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   lkv.init(wave, lane, kvstride);
   auto stage = [&](int kvs, int slot) __attribute__((always_inline)) {
     __bf16 *Ks = lds + slot * C::BUF;
+    const uint32_t ka = lds0 + slot * C::BUF * 2;  // its LDS byte address
     const int64_t off = ((int64_t)(seq_off + kvs) * hkv + g) * D;
-    lkv.template stage<kRowTile>(Ks, kg + off, ke - kvs);
-    lkv.template stage<kColTile>(Ks + C::TSZ, vg + off, ke - kvs);
+    lkv.template stage<kRowTile>(Ks, ka, kg + off, ke - kvs);
+    lkv.template stage<kColTile>(Ks + C::TSZ, ka + C::TSZ * 2, vg + off, ke - kvs);
   };
 
   const float c2 = a.scale_log2;
@@ -212,17 +214,21 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
       // interior tiles carry no per-element compares)
       const bool need_mask = (kv0 + C::BN - 1 > rw0) || (kv0 + C::BN > k_hi);
       if (need_mask) {
+        // Key kv0 + 8lg + c (c = 32kp + 4ab + i) is visible to row qrow iff
+        // c <= min(qrow, k_hi - 1) - kv0 - 8lg =: lim.  The sign of lim - c
+        // picks +inf or -inf and min() applies it: no per-element compares,
+        // each of which would hold a scalar register pair.
 #pragma unroll
         for (int nq = 0; nq < C::NQ; ++nq) {
-          const int qrow = rw0 + 16 * nq + l16;
+          const int lim = min(rw0 + 16 * nq + l16, k_hi - 1) - kv0 - 8 * lg;
 #pragma unroll
           for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
             for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int kv = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
-                if (kv > qrow || kv >= k_hi) s[nq][kp][ab][i] = kNegInf;
+                const uint32_t sign = (uint32_t)(lim - (32 * kp + 4 * ab + i)) & 0x80000000u;
+                s[nq][kp][ab][i] = fminf(s[nq][kp][ab][i], __builtin_bit_cast(float, sign | 0x7f800000u));
               }
         }
       }

@@ -55,7 +55,8 @@ struct FwdArgs {
   int32_t merge;         // 1: merge into the fp32 (O, LSE) already in o/lse
 };
 
-// D[h][t] = <dO[t,h,:], O[t,h,:]> for every token row.
+// delta[h][t] = -D = -<dO[t,h,:], O[t,h,:]> for every token row (negated: the
+// backward's products dP = dO V^T start from it and yield dP - D directly).
 struct PreArgs {
   const void *o, *d_o;
   float *delta;

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
     if (c == 0) {
       const int64_t t = row / a.hq;
       const int h = (int)(row - t * a.hq);
-      a.delta[(int64_t)h * a.tokens + t] = acc;
+      a.delta[(int64_t)h * a.tokens + t] = -acc;  // stored negated: the backward's start value of dP
     }
   }
 }

@@ -45,17 +45,25 @@ namespace dev {
 
 constexpr int kTileRows = 64;
 
+// LDS byte address of a pointer into a __shared__ array.  Kernels take it
+// once from the array itself and add compile-time offsets: converting
+// computed generic pointers instead costs a null check per use and keeps
+// 64-bit pointers in scalar registers.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
 // Direct copy global -> LDS of BYTES (4 or 16) per lane: lane i's bytes at
-// src (its own address) land at lds_dst + BYTES * i.  M0 holds the
-// wave-uniform LDS destination; no instruction the compiler generates in
-// these kernels keeps a value in M0, so clobbering it here is safe.
+// src (its own address) land at LDS byte address lds_dst + BYTES * i.  M0
+// holds the wave-uniform LDS destination; no instruction the compiler
+// generates in these kernels keeps a value in M0, so clobbering it here is
+// safe.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(const void *src, const void *lds_dst) {
+__device__ __forceinline__ void dma_to_lds(const void *src, uint32_t lds_dst) {
   static_assert(BYTES == 4 || BYTES == 16, "copy width");
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds_dst);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
   if constexpr (BYTES == 16)
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
   else
@@ -130,7 +138,8 @@ __device__ __forceinline__ bf16x8 lds_col8(const void *base, int byte_off) {
 // Rows >= nvalid are filled from row nvalid-1 (bf16 path) or with zeros
 // (fp32 path); the kernels mask them, they only need to be finite.
 //   init(): stride = elements between consecutive rows of the tensor;
-//   stage<KIND>(): src = first row of the tile; KIND = tile layout.
+//   stage<KIND>(): tile = the tile in LDS, as a pointer and as its LDS byte
+//   address; src = first row of the tile; KIND = tile layout.
 // bf16: stage() starts kInstr direct global->LDS copies per wavefront and
 //   returns; wait_vm / wait_stages below wait for them before the barrier
 //   that publishes the tile.
@@ -161,13 +170,14 @@ struct TileLoader<D, __bf16, W> {
     }
   }
   template <int KIND>
-  __device__ __forceinline__ void stage(__bf16 *tile, const __bf16 *src, int nvalid) const {
+  __device__ __forceinline__ void stage(__bf16 *, uint32_t tile, const __bf16 *src, int nvalid) const {
+    // One wave-uniform test per tile: full tiles use the precomputed offsets
+    // as they are; rows >= nvalid of a partial tile repeat the last valid row.
+    const bool partial = nvalid < kTileRows;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      int off = off_[KIND][t];
-      if (nvalid < kTileRows && row_[t] >= nvalid)  // partial tile: repeat the last valid row
-        off += (nvalid - 1 - row_[t]) * stride_;
-      dma_to_lds<16>(src + off, tile + (wave_ * NI + t) * RPI * D);
+      const int off = partial ? off_[KIND][t] + min(0, nvalid - 1 - row_[t]) * stride_ : off_[KIND][t];
+      dma_to_lds<16>(src + off, tile + (wave_ * NI + t) * RPI * D * 2);
     }
   }
 };
@@ -184,7 +194,7 @@ struct TileLoader<D, float, W> {
     tid_ = wave * 64 + lane;
   }
   template <int KIND>
-  __device__ __forceinline__ void stage(__bf16 *tile, const float *src, int nvalid) const {
+  __device__ __forceinline__ void stage(__bf16 *tile, uint32_t, const float *src, int nvalid) const {
     u32x4 r[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -201,8 +211,8 @@ struct TileLoader<D, float, W> {
 };
 
 // 64 consecutive floats (one per lane; lanes >= nvalid repeat element
-// nvalid-1) copied straight into LDS by one wavefront.
-__device__ __forceinline__ void stage_row_floats(float *dst, const float *src, int nvalid, int lane) {
+// nvalid-1) copied straight into LDS (byte address dst) by one wavefront.
+__device__ __forceinline__ void stage_row_floats(uint32_t dst, const float *src, int nvalid, int lane) {
   dma_to_lds<4>(src + min(lane, nvalid - 1), dst);
 }
 

@@ -121,9 +121,9 @@ def test_preprocess_then_d_ready():
     shape = sa.make_shape(q, k)
     ws = torch.empty(sa.segattn_bwd_workspace(shape, items), dtype=torch.uint8, device=DEV)
     sa.segattn_bwd_preprocess(q, k, o, do, items, ws)
-    # D rows are plain dot products of the kernel's inputs
+    # D rows are plain dot products of the kernel's inputs, stored negated
     delta = ws[: hq * T * 4].view(torch.float32).view(hq, T)
-    want = (o.float() * do.float()).sum(-1).transpose(0, 1)
+    want = -(o.float() * do.float()).sum(-1).transpose(0, 1)
     np.testing.assert_allclose(host64(delta), host64(want), rtol=1e-4, atol=1e-4)
     g1 = sa.segattn_bwd(q, k, v, o, lse, do, items, workspace=ws, d_ready=True, g_dtype=torch.float32)
     g2 = sa.segattn_bwd(q, k, v, o, lse, do, items, g_dtype=torch.float32)
