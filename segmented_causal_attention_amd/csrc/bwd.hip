@@ -376,18 +376,26 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
               const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[bv][0][32 * qp + 8 * lg + 4]) * -kLog2e;
 #pragma unroll
               for (int nk = 0; nk < 2; ++nk) {
+                // Row q = qt0 + 8lg + c (c = 32qp + 4ab + i) sees key `key` iff
+                // key - qt0 - 8lg <= c <= q_hi - 1 - qt0 - 8lg and k_lo <= key < k_hi:
+                // all of (c - c_lo), (c_hi - c) and kin are >= 0.  Their sign bit
+                // picks a +inf / -inf bound for the exponent's argument (no
+                // per-element compares, which would hold scalar register pairs).
                 const int key = kw0 + 16 * nk + l16;
+                const int c_lo = key - qt0 - 8 * lg, c_hi = q_hi - 1 - qt0 - 8 * lg;
+                const int kin = (key - k_lo) | (k_hi - 1 - key);
                 f32x4 pv[2];
 #pragma unroll
                 for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    float p = fast_exp2(fmaf(xs[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]));
+                    float arg = fmaf(xs[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]);
                     if constexpr (decltype(maskc)::value) {
-                      const int q = qt0 + 32 * qp + 8 * lg + 4 * ab + i;
-                      if (key > q || key < k_lo || key >= k_hi || q >= q_hi) p = 0.f;
+                      const int c = 32 * qp + 4 * ab + i;
+                      const uint32_t sign = (uint32_t)((c - c_lo) | (c_hi - c) | kin) & 0x80000000u;
+                      arg = fminf(arg, __builtin_bit_cast(float, sign | 0x7f800000u));
                     }
-                    pv[ab][i] = p;
+                    pv[ab][i] = fast_exp2(arg);
                   }
                 opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
                 *reinterpret_cast<bf16x8 *>(pshare[bv % NP][kgrp][qp][nk][lane]) = opa[qp][nk];
@@ -664,11 +672,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
             for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                float pv = fast_exp2(fmaf(s[nq][ab][i], c2, -lse2[nq]));
+                float arg = fmaf(s[nq][ab][i], c2, -lse2[nq]);
                 if constexpr (decltype(maskc)::value) {
-                  const int key = kv0 + 32 * kp + 8 * lg + 4 * ab + i;
-                  if (key > qrow || key >= k_hi) pv = 0.f;
+                  // key kv0 + 32kp + 8lg + c (c = 4ab + i) is visible iff
+                  // c <= min(qrow, k_hi - 1) - kv0 - 32kp - 8lg: the sign of
+                  // the difference picks a +inf / -inf bound (no compares)
+                  const int lim = min(qrow, k_hi - 1) - kv0 - 32 * kp - 8 * lg;
+                  const uint32_t sign = (uint32_t)(lim - (4 * ab + i)) & 0x80000000u;
+                  arg = fminf(arg, __builtin_bit_cast(float, sign | 0x7f800000u));
                 }
+                const float pv = fast_exp2(arg);
                 ds[ab][i] = pv * dp[nq][ab][i];
               }
             dsb[nq][kp] = pack_bf16x8(ds[0], ds[1]);

@@ -54,20 +54,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // Direct copy global -> LDS of BYTES (4 or 16) per lane: lane i's bytes at
-// src (its own address) land at LDS byte address lds_dst + BYTES * i.  M0
-// holds the wave-uniform LDS destination; no instruction the compiler
-// generates in these kernels keeps a value in M0, so clobbering it here is
-// safe.
+// base + voff (base wave-uniform, held in scalar registers; voff the lane's
+// byte offset) land at LDS byte address lds_dst + BYTES * i.  With the base
+// in scalar registers a copy needs no per-lane address arithmetic.  M0 holds
+// the wave-uniform LDS destination; no instruction the compiler generates in
+// these kernels keeps a value in M0, so clobbering it here is safe.  ALT
+// only changes the assembly text (a comment), so that the compiler does not
+// merge copies on different paths into one with selected operands.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(const void *src, uint32_t lds_dst) {
+template <int BYTES, bool ALT = false>
+__device__ __forceinline__ void dma_to_lds(const void *base, uint32_t voff, uint32_t lds_dst) {
   static_assert(BYTES == 4 || BYTES == 16, "copy width");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+  if constexpr (BYTES == 16 && !ALT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "memory", "m0");
+  else if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 ; partial" ::"s"(m0), "v"(voff), "s"(base)
+                 : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -155,29 +161,32 @@ struct TileLoader<D, __bf16, W> {
   static constexpr int NI = kTileRows / RPI / W;  // instructions per wavefront
   static constexpr int kInstr = NI;
   static_assert(NI >= 1 && NI * RPI * W == kTileRows, "tile split");
-  int row_[NI];     // lane's tile row per instruction
-  int off_[2][NI];  // element offset of the lane's chunk in a full tile, per tile kind
-  int stride_;      // elements between rows (64 * stride < 2^31: heads <= 65536, d <= 128)
-  int wave_;        // wavefront index (scalar)
+  int row_[NI];          // lane's tile row per instruction
+  uint32_t boff_[2][NI];  // byte offset of the lane's chunk in a full tile, per tile kind
+  uint32_t rbytes_;       // bytes between rows (64 rows < 2^32 bytes: heads <= 65536, d <= 128)
+  int wave_;              // wavefront index (scalar)
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
-    stride_ = (int)stride;
+    rbytes_ = 2u * (uint32_t)stride;
     wave_ = wave;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       row_[t] = (wave * NI + t) * RPI + lane / CPR;
-      off_[kRowTile][t] = row_[t] * stride_ + 8 * ((lane % CPR) ^ swz<D, kRowTile>(row_[t]));
-      off_[kColTile][t] = row_[t] * stride_ + 8 * ((lane % CPR) ^ swz<D, kColTile>(row_[t]));
+      boff_[kRowTile][t] = row_[t] * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kRowTile>(row_[t]));
+      boff_[kColTile][t] = row_[t] * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kColTile>(row_[t]));
     }
   }
   template <int KIND>
   __device__ __forceinline__ void stage(__bf16 *, uint32_t tile, const __bf16 *src, int nvalid) const {
-    // One wave-uniform test per tile: full tiles use the precomputed offsets
-    // as they are; rows >= nvalid of a partial tile repeat the last valid row.
-    const bool partial = nvalid < kTileRows;
+    if (nvalid >= kTileRows) {
+      // full tile: the precomputed lane offsets as they are
 #pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      const int off = partial ? off_[KIND][t] + min(0, nvalid - 1 - row_[t]) * stride_ : off_[KIND][t];
-      dma_to_lds<16>(src + off, tile + (wave_ * NI + t) * RPI * D * 2);
+      for (int t = 0; t < NI; ++t) dma_to_lds<16>(src, boff_[KIND][t], tile + (wave_ * NI + t) * RPI * D * 2);
+    } else {
+      // partial tile: rows >= nvalid repeat the last valid row
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+        dma_to_lds<16, true>(src, boff_[KIND][t] - (uint32_t)max(0, row_[t] - (nvalid - 1)) * rbytes_,
+                             tile + (wave_ * NI + t) * RPI * D * 2);
     }
   }
 };
@@ -213,7 +222,7 @@ struct TileLoader<D, float, W> {
 // 64 consecutive floats (one per lane; lanes >= nvalid repeat element
 // nvalid-1) copied straight into LDS (byte address dst) by one wavefront.
 __device__ __forceinline__ void stage_row_floats(uint32_t dst, const float *src, int nvalid, int lane) {
-  dma_to_lds<4>(src + min(lane, nvalid - 1), dst);
+  dma_to_lds<4>(src, 4u * (uint32_t)min(lane, nvalid - 1), dst);
 }
 
 // Waits until at most N of this wavefront's vector memory operations are
