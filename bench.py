@@ -2,6 +2,13 @@
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu-baseline]
                     [--no-hbm-kernels]
+    python bench.py --sweep-segments
+
+--sweep-segments times the same fwd+bwd path on 131072 tokens (32 heads,
+d = 128, bf16) cut into N equal-length segments, N = 1, 2, 4, ..., 1024, each
+segment's queries attending to the whole resident prefix: the segment-length
+sweep of SPPO section 4 (Figure 7) on this GPU.  It prints one JSON line per
+N instead of the single benchmark line.
 
 One step = one pass of the whole path over one synthetic batch, inputs resident
 in HBM: the host planner cuts the sequence into FLOPs-balanced segments, the
@@ -81,6 +88,8 @@ def parse():
                    help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
                    help="token prefix of one head timed for the CPU oracle baseline")
+    p.add_argument("--sweep-segments", action="store_true",
+                   help="time fwd+bwd over 131072 tokens in N = 1..1024 equal segments (one line per N)")
     return p.parse_args()
 
 
@@ -273,6 +282,48 @@ def hbm_kernels(torch, sa, W):
     return out
 
 
+def segment_sweep(torch, sa, synth, max_segments=1024, warmup=1, steps=3):
+    """Segment-length sweep: N equal-length segments of one 131072-token
+    sequence, segment i's queries [i s, (i+1) s) against keys [0, (i+1) s).
+    The visible pairs (and so the algorithmic FLOPs) are the same for every
+    N; only the tiling changes.  One JSON line per N."""
+    S, hq, d = 131072, 32, 128
+    t = synth.gen_tensors(1003, S, hq, hq, d, dtype="bf16", device="cuda")
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty((S, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, S), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    shape = sa.make_shape(q, k)
+    flops = 14 * d * visible_pairs([S]) * hq
+    E = torch.cuda.Event
+    N = 1
+    while N <= max_segments:
+        s = S // N
+        items = np.array([[0, i * s, (i + 1) * s, 0, (i + 1) * s] for i in range(N)], np.int64)
+        rev = items[::-1].copy()
+        fws = torch.empty(max(sa.segattn_fwd_workspace(shape, items), 16), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(sa.segattn_bwd_workspace(shape, rev), dtype=torch.uint8, device="cuda")
+        fwd_ms, bwd_ms = [], []
+        for it in range(warmup + steps):
+            ev = [E(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws)
+            ev[1].record()
+            sa.segattn_bwd(q, k, v, o, lse, do, rev, dq=dq, dk=dk, dv=dv, workspace=bws)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if it >= warmup:
+                fwd_ms.append(ev[0].elapsed_time(ev[1]))
+                bwd_ms.append(ev[1].elapsed_time(ev[2]))
+        f, b = float(np.median(fwd_ms)), float(np.median(bwd_ms))
+        print(json.dumps({"sweep": "segment_length", "tokens": S, "heads": hq, "head_dim": d, "segments": N,
+                          "segment_len": s, "fwd_ms": round(f, 3), "bwd_ms": round(b, 3),
+                          "total_ms": round(f + b, 3), "tflops": round(flops / ((f + b) * 1e-3) / 1e12, 1),
+                          "pct_of_bf16_peak": round(100 * flops / ((f + b) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}),
+              flush=True)
+        N *= 2
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -285,6 +336,9 @@ def main():
     import synthetic_inputs as synth
 
     torch.cuda.set_device(0)
+    if args.sweep_segments:
+        segment_sweep(torch, sa, synth)
+        return
     W = Workload(args.workload, torch, sa, synth)
     stream = torch.cuda.current_stream()
 
