@@ -14,6 +14,8 @@ attention  -- causal softmax attention forward / backward in float64, the
               log-sum-exp merge of partial results, and the segmented
               (item-by-item) evaluation used to check the identity
               "segmented + merged == unsegmented".
+offload    -- the sequence-aware offload plan (ratios alpha_i and the GPU
+              memory recurrence) in float64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, library routines, finite differences and exact
@@ -41,3 +43,4 @@ from .attention import (  # noqa: F401
     attention_rows_bwd,
     attention_keys_bwd,
 )
+from .offload import plan_offload, offload_rows  # noqa: F401,E402
