@@ -3,12 +3,19 @@
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu-baseline]
                     [--no-hbm-kernels]
     python bench.py --sweep-segments
+    python bench.py --offload
 
 --sweep-segments times the same fwd+bwd path on 131072 tokens (32 heads,
 d = 128, bf16) cut into N equal-length segments, N = 1, 2, 4, ..., 1024, each
 segment's queries attending to the whole resident prefix: the segment-length
 sweep of SPPO section 4 (Figure 7) on this GPU.  It prints one JSON line per
 N instead of the single benchmark line.
+
+--offload measures sequence-aware offloading (SPPO sections 5.1-5.2) on the
+default workload, and prints one JSON line with the result.  The forward and
+backward run per segment.  After segment i's forward, the planned share of
+its backward-only rows (Q, O, LSE) is copied to pinned host memory on a
+second stream; before its backward they are copied back.
 
 One step = one pass of the whole path over one synthetic batch, inputs resident
 in HBM: the host planner cuts the sequence into FLOPs-balanced segments, the
@@ -88,6 +95,8 @@ def parse():
                    help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
                    help="token prefix of one head timed for the CPU oracle baseline")
+    p.add_argument("--offload", action="store_true",
+                   help="per-segment fwd/bwd with Q/O/LSE offloaded to host memory and prefetched (one line)")
     p.add_argument("--sweep-segments", action="store_true",
                    help="time fwd+bwd over 131072 tokens in N = 1..1024 equal segments (one line per N)")
     return p.parse_args()
@@ -324,6 +333,138 @@ def segment_sweep(torch, sa, synth, max_segments=1024, warmup=1, steps=3):
         N *= 2
 
 
+def offload_bench(torch, sa, synth, reps=5):
+    """Sequence-aware offloading on the 32768-token workload (8 FLOPs-
+    balanced segments).  Three per-step timings: the one-launch path, the
+    per-segment schedule, and the per-segment schedule with offloading; plus
+    the device -> host bandwidth that sets the per-stage transfer volume
+    (threshold = bandwidth x one balanced segment's forward time)."""
+    W = Workload("c2", torch, sa, synth)
+    T, hq, d = W.T, W.hq, W.d
+    b = [int(x) for x in sa.segattn_partition(T, W.w["N"])]
+    N = len(b) - 1
+    L = [b[i + 1] - b[i] for i in range(N)]
+    items = [np.array([[0, b[i], b[i + 1], 0, b[i + 1]]], np.int64) for i in range(N)]
+    q = W.q.clone()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+    grads = [torch.zeros(x.shape, dtype=torch.float32, device="cuda") for x in (q, W.k, W.v)]
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    E = torch.cuda.Event
+    row_bytes = hq * d * 2 + hq * d * 2 + hq * 4  # Q row + O row (bf16) + LSE entries
+    # device -> host bandwidth into pinned memory (one 256 MiB copy, after a warm-up)
+    cal_d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    cal_h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    for _ in range(2):
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        e0.record(copy)
+        sa.segattn_copy_rows(cal_h.view(1, -1), cal_d.view(1, -1), stream=copy)
+        e1.record(copy)
+        torch.cuda.synchronize()
+    bw_d2h = cal_d.numel() / (e0.elapsed_time(e1) * 1e-3)
+    hostbuf = [(torch.empty((L[i], hq, d), dtype=torch.bfloat16, pin_memory=True),
+                torch.empty((L[i], hq, d), dtype=torch.bfloat16, pin_memory=True),
+                torch.empty((hq, L[i]), dtype=torch.float32, pin_memory=True)) for i in range(N)]
+    order_ev = [E() for _ in range(N)]
+    for e in order_ev:
+        e.record(comp)
+
+    def step(moved, ev):
+        """One fwd+bwd step; moved[i] rows of segment i go to host and back.
+        ev: 4 timing events (fwd start / end, bwd start / end) on comp."""
+        for g in grads:
+            g.zero_()
+        ev[0].record(comp)
+        ce = []
+        for i in range(N):
+            sa.segattn_fwd(q, W.k, W.v, items[i], o=o, lse=lse)
+            if moved[i] > 0:
+                lo, r = b[i], moved[i]
+                hq_, ho, hs = hostbuf[i]
+                sa.segattn_stream_order(order_ev[i], comp, copy)
+                c0 = E(enable_timing=True)
+                c0.record(copy)
+                sa.segattn_copy_rows(hq_[:r], q[lo:lo + r], stream=copy)
+                sa.segattn_copy_rows(ho[:r], o[lo:lo + r], stream=copy)
+                sa.segattn_copy_rows(hs[:, :r], lse[:, lo:lo + r], stream=copy)
+                c1 = E(enable_timing=True)
+                c1.record(copy)
+                ce.append((c0, c1, r))
+        ev[1].record(comp)
+        ready = {}
+        pe = []
+        for i in reversed(range(N)):
+            if moved[i] > 0:
+                lo, r = b[i], moved[i]
+                hq_, ho, hs = hostbuf[i]
+                p0 = E(enable_timing=True)
+                p0.record(copy)
+                sa.segattn_copy_rows(q[lo:lo + r], hq_[:r], stream=copy)
+                sa.segattn_copy_rows(o[lo:lo + r], ho[:r], stream=copy)
+                sa.segattn_copy_rows(lse[:, lo:lo + r], hs[:, :r], stream=copy)
+                ready[i] = E(enable_timing=True)
+                ready[i].record(copy)
+                pe.append((p0, ready[i], r))
+        ev[2].record(comp)
+        for i in reversed(range(N)):
+            if i in ready:
+                comp.wait_event(ready[i])
+            sa.segattn_bwd(q, W.k, W.v, o, lse, W.do, items[i], dq=grads[0], dk=grads[1], dv=grads[2],
+                           accumulate=True)
+        ev[3].record(comp)
+        return ce, pe
+
+    def timed(moved):
+        fw, bw, d2h, h2d = [], [], [], []
+        for it in range(1 + reps):
+            ev = [E(enable_timing=True) for _ in range(4)]
+            ce, pe = step(moved, ev)
+            torch.cuda.synchronize()
+            if it == 0:
+                continue
+            fw.append(ev[0].elapsed_time(ev[1]))
+            bw.append(ev[2].elapsed_time(ev[3]))
+            if ce:
+                d2h.append(sum(r for *_, r in ce) * row_bytes / (sum(c0.elapsed_time(c1) for c0, c1, _ in ce) * 1e-3))
+                h2d.append(sum(r for *_, r in pe) * row_bytes / (sum(p0.elapsed_time(p1) for p0, p1, _ in pe) * 1e-3))
+        med = lambda x: float(np.median(x)) if x else None
+        return med(fw), med(bw), med(d2h), med(h2d)
+
+    # one-launch path (the benchmark's step) for reference
+    one = []
+    for it in range(1 + reps):
+        ev = [E(enable_timing=True) for _ in range(4)]
+        run_step(W, torch, ev)
+        torch.cuda.synchronize()
+        if it:
+            one.append(ev[0].elapsed_time(ev[3]))
+    none = [0] * N
+    f0, b0, _, _ = timed(none)
+    ref = [g.clone() for g in grads]
+    seg_fwd_ms = f0 / N
+    threshold = bw_d2h * seg_fwd_ms * 1e-3
+    alpha, moved, mem, peak = sa.segattn_offload_plan(L, row_bytes, threshold)
+    moved = [int(x) for x in moved]
+    moved[-1] = 0  # the last segment's backward runs first
+    f1, b1, d2h, h2d = timed(moved)
+    same = all(torch.equal(a, g) for a, g in zip(ref, grads))
+    moved_bytes = sum(moved) * row_bytes
+    print(json.dumps({
+        "offload": "sequence_aware", "workload": "S32768_H32_d128_N8_bf16", "segments": N,
+        "segment_lengths": L, "row_bytes": row_bytes,
+        "d2h_calibration_GBs": round(bw_d2h / 1e9, 2), "threshold_bytes": int(threshold),
+        "alpha": [round(float(a), 4) for a in alpha], "rows_moved": moved,
+        "moved_bytes": int(moved_bytes), "backward_only_bytes": int(sum(L) * row_bytes),
+        "plan_peak_bytes": int(peak),
+        "one_launch_ms": round(float(np.median(one)), 3),
+        "per_segment_ms": {"fwd": round(f0, 3), "bwd": round(b0, 3), "total": round(f0 + b0, 3)},
+        "offload_ms": {"fwd": round(f1, 3), "bwd": round(b1, 3), "total": round(f1 + b1, 3)},
+        "exposed_ms": round((f1 + b1) - (f0 + b0), 3),
+        "d2h_GBs": round(d2h / 1e9, 2) if d2h else None, "h2d_GBs": round(h2d / 1e9, 2) if h2d else None,
+        "grads_bit_identical": bool(same)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -338,6 +479,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep_segments:
         segment_sweep(torch, sa, synth)
+        return
+    if args.offload:
+        offload_bench(torch, sa, synth)
         return
     W = Workload(args.workload, torch, sa, synth)
     stream = torch.cuda.current_stream()

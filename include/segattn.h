@@ -199,6 +199,49 @@ int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const 
                 const segattn_item *items, int32_t n_items, void *dq, void *dk, void *dv,
                 int32_t g_dtype, uint32_t flags, void *workspace, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- offload
+ * Moving a subsequence's backward-only activations to host memory while the
+ * next subsequence computes (SPPO section 5.1, two-level activation
+ * management: keys and values stay resident because later subsequences
+ * attend to them; section 5.2, sequence-aware offloading).  For attention
+ * the backward-only tensors of a segment are its Q and O rows and its LSE
+ * entries.  The library plans and copies; the caller owns every buffer and
+ * decides when device rows may be released or overwritten. */
+
+/* Copy directions of segattn_copy_rows. */
+#define SEGATTN_D2H 0 /* device -> host */
+#define SEGATTN_H2D 1 /* host -> device */
+
+/* Offload plan of n subsequences, subsequence i holding rows[i] rows of
+ * row_bytes[i] bytes (A_i = rows[i] * row_bytes[i], exact in int64 then
+ * converted to double).  SPPO section 5.2: each stage moves the same volume,
+ * alpha_i A_i = threshold_bytes, so alpha_i = min(1, threshold / A_i)
+ * (0 when A_i = 0); rows_moved[i] = floor(alpha_i * rows[i]) whole rows; the
+ * GPU memory after stage i is M_0 = A_0, M_i = M_{i-1} + A_i - alpha_{i-1}
+ * A_{i-1}, and *peak_bytes = max_i M_i.  Double arithmetic, in that order.
+ * alpha, rows_moved, mem_bytes: HOST arrays of n entries; peak_bytes may be
+ * NULL.  Errors: E_INVALID (NULL arrays, n < 1, threshold not finite and
+ * > 0, a negative rows or row_bytes, or an int64 overflow in A_i). */
+int segattn_offload_plan(const int64_t *rows, const int64_t *row_bytes, int32_t n, double threshold_bytes,
+                         double *alpha, int64_t *rows_moved, double *mem_bytes, double *peak_bytes);
+
+/* Copies `rows` rows of `row_bytes` bytes, row r from src + r*src_pitch to
+ * dst + r*dst_pitch, asynchronously on `stream` (a hipStream_t, NULL = the
+ * null stream).  kind SEGATTN_D2H: src device, dst host; SEGATTN_H2D: src
+ * host, dst device.  The host side should be pinned memory (from
+ * hipHostMalloc) for the copy to run beside kernels.  Pitches >= row_bytes.
+ * rows == 0 or row_bytes == 0 is a no-op.  Errors: E_INVALID (NULL pointer
+ * with a non-empty copy, bad kind, negative sizes, pitch < row_bytes),
+ * E_DEVICE. */
+int segattn_copy_rows(void *dst, int64_t dst_pitch, const void *src, int64_t src_pitch, int64_t row_bytes,
+                      int64_t rows, int32_t kind, void *stream);
+
+/* Makes to_stream wait, without blocking the host, for all work enqueued on
+ * from_stream so far: records `event` (a hipEvent_t owned by the caller) on
+ * from_stream and makes to_stream wait for it.  Errors: E_INVALID (NULL
+ * event), E_DEVICE. */
+int segattn_stream_order(void *event, void *from_stream, void *to_stream);
+
 /* ------------------------------------------------------------- diagnostics */
 
 /* Static name of a status code ("SEGATTN_OK", ...). */

@@ -12,11 +12,14 @@ from .binding import (  # noqa: F401
     segattn_bwd,
     segattn_bwd_preprocess,
     segattn_bwd_workspace,
+    segattn_copy_rows,
     segattn_fwd,
     segattn_fwd_workspace,
     segattn_merge,
+    segattn_offload_plan,
     segattn_partition,
     segattn_partition_varlen,
     segattn_ring_items,
+    segattn_stream_order,
     segattn_version,
 )

@@ -26,6 +26,9 @@ SEGATTN_MERGE_INTO = 1
 SEGATTN_ACCUMULATE = 2
 SEGATTN_D_READY = 4
 
+SEGATTN_D2H = 0
+SEGATTN_H2D = 1
+
 # Every symbol declared in include/segattn.h.
 EXPORTS = (
     "segattn_partition",
@@ -36,6 +39,9 @@ EXPORTS = (
     "segattn_merge",
     "segattn_bwd_workspace",
     "segattn_bwd_preprocess",
+    "segattn_offload_plan",
+    "segattn_copy_rows",
+    "segattn_stream_order",
     "segattn_bwd",
     "segattn_status_string",
     "segattn_last_error",
@@ -86,6 +92,10 @@ def lib():
     L.segattn_bwd_preprocess.argtypes = [P(Shape), vp, i32, vp, P(Item), i32, vp, sz, vp]
     L.segattn_bwd.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, P(Item), i32, vp, vp, vp, i32,
                               ctypes.c_uint32, vp, sz, vp]
+    f64 = ctypes.c_double
+    L.segattn_offload_plan.argtypes = [P(i64), P(i64), i32, f64, P(f64), P(i64), P(f64), P(f64)]
+    L.segattn_copy_rows.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]
+    L.segattn_stream_order.argtypes = [vp, vp, vp]
     for name in EXPORTS:
         fn = getattr(L, name)
         if name in ("segattn_status_string", "segattn_last_error", "segattn_version"):

@@ -195,5 +195,67 @@ def segattn_bwd(q, k, v, o, lse, do, items, *, scale=None, dq=None, dk=None, dv=
     return dq, dk, dv
 
 
+# ------------------------------------------------------------------ offload
+
+def segattn_offload_plan(rows, row_bytes, threshold_bytes):
+    """Offload plan of the subsequences (rows[i] rows of row_bytes[i] bytes
+    each) for a per-stage transfer volume: returns (alpha, rows_moved, mem,
+    peak) as numpy float64 / int64 arrays and a float."""
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(row_bytes, dtype=np.int64), r.shape))
+    n = r.shape[0]
+    alpha = np.zeros(n, np.float64)
+    moved = np.zeros(n, np.int64)
+    mem = np.zeros(n, np.float64)
+    peak = ctypes.c_double(0.0)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    check(lib().segattn_offload_plan(r.ctypes.data_as(_I64P), b.ctypes.data_as(_I64P), n, float(threshold_bytes),
+                                     alpha.ctypes.data_as(f64p), moved.ctypes.data_as(_I64P),
+                                     mem.ctypes.data_as(f64p), ctypes.byref(peak)))
+    return alpha, moved, mem, peak.value
+
+
+def _rows_view(t, name):
+    """(pointer, rows, row bytes, pitch) of a tensor whose dim-0 slices are
+    contiguous rows (a slice of a token-major tensor, or a [heads, tokens]
+    column block)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() == 0:
+        raise ValueError(f"{name} must have a row dimension")
+    inner = t[0] if t.shape[0] > 0 else t.reshape(-1)
+    if t.shape[0] > 0 and not inner.is_contiguous():
+        raise ValueError(f"{name}: each row must be contiguous")
+    row_bytes = (inner.numel() if t.shape[0] > 0 else 0) * t.element_size()
+    pitch = t.stride(0) * t.element_size() if t.shape[0] > 1 else row_bytes
+    return ctypes.c_void_p(t.data_ptr()), t.shape[0], row_bytes, pitch
+
+
+def segattn_copy_rows(dst, src, *, stream=None):
+    """Copies the rows of src into dst (same shape; one on the device, the
+    other in pinned host memory) asynchronously on `stream` (default: the
+    current stream).  The direction follows the devices of src and dst."""
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError("dst and src must have the same shape and dtype")
+    if src.is_cuda and not dst.is_cuda:
+        kind = _lib.SEGATTN_D2H
+    elif dst.is_cuda and not src.is_cuda:
+        kind = _lib.SEGATTN_H2D
+    else:
+        raise ValueError("one of dst / src must be a device tensor and the other a host tensor")
+    dp, rows, row_bytes, dpitch = _rows_view(dst, "dst")
+    sp, _, _, spitch = _rows_view(src, "src")
+    dev = src.device if src.is_cuda else dst.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    check(lib().segattn_copy_rows(dp, dpitch, sp, spitch, row_bytes, rows, kind, ctypes.c_void_p(s.cuda_stream)))
+
+
+def segattn_stream_order(event, from_stream, to_stream):
+    """Makes to_stream wait for the work enqueued on from_stream so far
+    (event: a torch.cuda.Event, recorded on from_stream)."""
+    check(lib().segattn_stream_order(ctypes.c_void_p(event.cuda_event), ctypes.c_void_p(from_stream.cuda_stream),
+                                     ctypes.c_void_p(to_stream.cuda_stream)))
+
+
 def segattn_version():
     return lib().segattn_version().decode()

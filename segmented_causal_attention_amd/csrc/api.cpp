@@ -424,3 +424,35 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   if (hipError_t e = launch_bwd(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
   return SEGATTN_OK;
 }
+
+// ------------------------------------------------------------------ offload
+// Row copies and stream ordering for moving backward-only activations to
+// host memory beside the computation (SPPO sections 5.1-5.2).
+extern "C" int segattn_copy_rows(void *dst, int64_t dst_pitch, const void *src, int64_t src_pitch,
+                                 int64_t row_bytes, int64_t rows, int32_t kind, void *stream) {
+  clear_error();
+  static const char *fn = "segattn_copy_rows";
+  if (kind != SEGATTN_D2H && kind != SEGATTN_H2D) return fail(SEGATTN_E_INVALID, "%s: bad kind %d", fn, kind);
+  if (rows < 0 || row_bytes < 0) return fail(SEGATTN_E_INVALID, "%s: negative size", fn);
+  if (rows == 0 || row_bytes == 0) return SEGATTN_OK;
+  if (!dst || !src) return fail(SEGATTN_E_INVALID, "%s: NULL pointer", fn);
+  if (dst_pitch < row_bytes || src_pitch < row_bytes)
+    return fail(SEGATTN_E_INVALID, "%s: pitch smaller than the row", fn);
+  const hipMemcpyKind k = kind == SEGATTN_D2H ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  hipError_t e;
+  if (rows == 1 || (dst_pitch == row_bytes && src_pitch == row_bytes))
+    e = hipMemcpyAsync(dst, src, (size_t)(row_bytes * rows), k, (hipStream_t)stream);
+  else
+    e = hipMemcpy2DAsync(dst, (size_t)dst_pitch, src, (size_t)src_pitch, (size_t)row_bytes, (size_t)rows, k,
+                         (hipStream_t)stream);
+  return e == hipSuccess ? SEGATTN_OK : device_error(e, fn);
+}
+
+extern "C" int segattn_stream_order(void *event, void *from_stream, void *to_stream) {
+  clear_error();
+  static const char *fn = "segattn_stream_order";
+  if (!event) return fail(SEGATTN_E_INVALID, "%s: NULL event", fn);
+  hipError_t e = hipEventRecord((hipEvent_t)event, (hipStream_t)from_stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent((hipStream_t)to_stream, (hipEvent_t)event, 0);
+  return e == hipSuccess ? SEGATTN_OK : device_error(e, fn);
+}

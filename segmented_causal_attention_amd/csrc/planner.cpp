@@ -213,6 +213,56 @@ extern "C" int segattn_ring_items(const int64_t *bounds, int32_t N, int64_t bloc
   return SEGATTN_OK;
 }
 
+// Offload plan: SPPO section 5.2 (sequence-aware offloading).  Every stage
+// moves the same volume, alpha_i A_i = threshold, so that the transfer takes
+// as long as one balanced computation step; the GPU memory after stage i is
+// M_i = M_{i-1} + A_i - alpha_{i-1} A_{i-1}.  The double operations below are
+// kept separate and uncontracted so their rounding is fixed.
+#pragma clang fp contract(off)
+extern "C" int segattn_offload_plan(const int64_t *rows, const int64_t *row_bytes, int32_t n,
+                                    double threshold_bytes, double *alpha, int64_t *rows_moved,
+                                    double *mem_bytes, double *peak_bytes) {
+  segattn::clear_error();
+  using segattn::fail;
+  if (!rows || !row_bytes || !alpha || !rows_moved || !mem_bytes)
+    return fail(SEGATTN_E_INVALID, "segattn_offload_plan: NULL array");
+  if (n < 1) return fail(SEGATTN_E_INVALID, "segattn_offload_plan: n = %d < 1", n);
+  if (!(threshold_bytes > 0.0) || !(threshold_bytes < 1e308))
+    return fail(SEGATTN_E_INVALID, "segattn_offload_plan: threshold must be finite and > 0");
+  for (int32_t i = 0; i < n; ++i) {
+    if (rows[i] < 0 || row_bytes[i] < 0)
+      return fail(SEGATTN_E_INVALID, "segattn_offload_plan: negative size at %d", i);
+    if (row_bytes[i] > 0 && rows[i] > INT64_MAX / row_bytes[i])
+      return fail(SEGATTN_E_INVALID, "segattn_offload_plan: rows * row_bytes overflows at %d", i);
+  }
+  double m = 0.0, peak = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double a = (double)(rows[i] * row_bytes[i]);
+    double r = 0.0;
+    if (a != 0.0) {
+      r = threshold_bytes / a;
+      if (r > 1.0) r = 1.0;
+    }
+    alpha[i] = r;
+    const double moved_rows = r * (double)rows[i];
+    int64_t k = (int64_t)moved_rows;  // floor: moved_rows >= 0
+    if (k > rows[i]) k = rows[i];
+    rows_moved[i] = k;
+    if (i == 0) {
+      m = a;
+    } else {
+      const double moved = alpha[i - 1] * (double)(rows[i - 1] * row_bytes[i - 1]);
+      m = m + a;
+      m = m - moved;
+    }
+    mem_bytes[i] = m;
+    if (i == 0 || m > peak) peak = m;
+  }
+  if (peak_bytes) *peak_bytes = peak;
+  return SEGATTN_OK;
+}
+#pragma clang fp contract(on)
+
 extern "C" const char *segattn_status_string(int status) {
   switch (status) {
     case SEGATTN_OK: return "SEGATTN_OK";
