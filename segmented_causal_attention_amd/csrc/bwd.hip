@@ -16,19 +16,21 @@
 // dK/dV role: key-stationary.  A workgroup owns 128 keys of one KV head in
 //   4 groups of 32; each group is handled by two wavefronts on one SIMD.  It
 //   walks every (item, query head of the group, 64-row query tile) that can
-//   see its keys.  Per tile, the dV wavefront computes S = Q K^T and P and
-//   hands P (bf16) to the dK wavefront through LDS while that one computes
-//   dP = dO V^T; after a barrier the first accumulates dV += P^T dO, the
-//   second dS = P (dP - D) and dK += dS^T Q.  Each wavefront keeps only its
-//   own key-side operand (K or V) and accumulator in registers, so two fit
-//   on every SIMD, and the two do equal MFMA work (4 products per tile).  Q
-//   and dO tiles are staged row-major; the operands contracted over query
-//   rows are read with transposing LDS reads.
+//   see its keys, one tile per barrier.  In iteration i the dV wavefront
+//   computes S = Q K^T and P of tile i, leaves P (bf16) in an LDS buffer and
+//   accumulates dV += P^T dO; the dK wavefront works one tile behind: dP =
+//   dO V^T of tile i-1 (its accumulators start from -D, so they hold
+//   dP - D), dS = P (dP - D) with the P left in iteration i-1, and dK +=
+//   dS^T Q.  Each wavefront keeps only its own key-side operand (K or V) and
+//   accumulator in registers, so two fit on every SIMD, and the two do equal
+//   MFMA work (2 products each per tile).  Q and dO tiles are staged once, in
+//   the column layout: row reads for the products over the head dim,
+//   transposing reads for those over query rows.
 // dQ role: query-stationary, like the forward.  A workgroup owns 256 query
-//   rows of one head (8 waves x 32 rows, two per SIMD; Q and dO in registers)
-//   and walks the
-//   64-key tiles of every item of its query group; per tile it recomputes
-//   S^T, P, dP^T, dS^T and accumulates dQ^T (3 products).
+//   rows of one head (8 wavefronts x 32 rows, two per SIMD; Q and dO in
+//   registers) and walks the 64-key tiles of every item of its query group;
+//   per tile it recomputes S^T, P, dP^T - D, dS^T and accumulates dQ^T
+//   (3 products).
 #include <type_traits>
 
 #include "device_common.h"

@@ -4,8 +4,8 @@
 // query head: 8 wavefronts x 32 rows, two wavefronts per SIMD, so one
 // wavefront's softmax overlaps the other's matrix products.  The item's
 // visible keys are streamed in 64-key tiles that global_load_lds copies
-// straight into swizzled LDS tiles (double buffered) while the query rows stay
-// in registers.  Scores are computed transposed, S^T = K Q^T, so that every
+// straight into swizzled LDS tiles (a ring of kFwdStages slots, copied up to
+// kFwdStages - 1 tiles ahead) while the query rows stay in registers.  Scores are computed transposed, S^T = K Q^T, so that every
 // lane owns one query row's scores: the row max needs only two cross-lane
 // steps, and the probabilities are already in the B-operand layout of the
 // second product O^T += V^T P^T, whose V^T operand comes from transposing LDS

@@ -11,11 +11,14 @@
 //     over rows; each half-wavefront visits rows 8g + b of g in {0,1} (or
 //     {2,3}), two chunks each, and needs eight disjoint 32-byte bank windows.
 //     swz = ((r >> 3) & 1) << 3 | (r & 3) << 1 | (r >> 4) & 1.
-// Both were measured bank-conflict free on the device (SQ_LDS_BANK_CONFLICT).
-// A tensor that is read both ways (Q and dO in the dK/dV kernel, K in the dQ
-// kernel) is staged once, in the column layout: its row reads then run at
-// about 60% of the row layout's LDS rate (measured), which costs far less
-// than copying the tile from memory twice.  For D = 64 (8 chunks per row) the
+// Each was measured bank-conflict free on the device for its own read
+// pattern (SQ_LDS_BANK_CONFLICT).  A tensor that is read both ways (Q and dO
+// in the dK/dV role, K in the dQ role) is staged once, in the column layout:
+// its row reads then conflict and run at about 60% of the row layout's LDS
+// rate, which costs far less than copying the tile from memory twice.  (XOR
+// swizzles that are conflict-free both ways exist -- a timed search over all
+// linear ones found many -- but removing those conflicts left the kernel
+// times unchanged, so the two layouts above stay.)  For D = 64 (8 chunks per row) the
 // swizzle is taken mod 8.  Without padding a wavefront fills 1 KB of a tile
 // with one global_load_lds_dwordx4 (global memory straight to LDS, no
 // registers).
