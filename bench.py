@@ -4,12 +4,17 @@
                     [--no-hbm-kernels]
     python bench.py --sweep-segments
     python bench.py --offload
+    python bench.py --latency-c1
 
 --sweep-segments times the same fwd+bwd path on 131072 tokens (32 heads,
 d = 128, bf16) cut into N equal-length segments, N = 1, 2, 4, ..., 1024, each
 segment's queries attending to the whole resident prefix: the segment-length
 sweep of SPPO section 4 (Figure 7) on this GPU.  It prints one JSON line per
 N instead of the single benchmark line.
+
+--latency-c1 times the small oracle-identity case (1024 tokens, one head,
+d = 64, fp32 inputs, 4 FLOPs-balanced segments, forward only), which is
+launch-bound: GPU time and host wall time per call, one JSON line.
 
 --offload measures sequence-aware offloading (SPPO sections 5.1-5.2) on the
 default workload, and prints one JSON line with the result.  The forward and
@@ -95,6 +100,8 @@ def parse():
                    help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
                    help="token prefix of one head timed for the CPU oracle baseline")
+    p.add_argument("--latency-c1", action="store_true",
+                   help="per-call latency of the 1024-token, 1-head, d=64 fp32 forward (one line)")
     p.add_argument("--offload", action="store_true",
                    help="per-segment fwd/bwd with Q/O/LSE offloaded to host memory and prefetched (one line)")
     p.add_argument("--sweep-segments", action="store_true",
@@ -333,6 +340,40 @@ def segment_sweep(torch, sa, synth, max_segments=1024, warmup=1, steps=3):
         N *= 2
 
 
+def c1_latency(torch, sa, synth, calls=500, warmup=50):
+    """Per-call latency of the forward over the 1024-token, one-head, d = 64
+    fp32 workload in 4 FLOPs-balanced segments (one segattn_fwd call with 4
+    items).  GPU time: HIP events around `calls` back-to-back calls on the
+    launch stream.  Host time: wall clock of the same calls, including the
+    host-side checks, table upload and launch, until the stream drains."""
+    w = synth.WORKLOADS["c1"]
+    S, N, d = w["S"], w["N"], w["d"]
+    t = synth.gen_tensors(w["seed"], S, w["hq"], w["hkv"], d, dtype="fp32", device="cuda")
+    q, k, v = t["q"], t["k"], t["v"]
+    b = [int(x) for x in sa.segattn_partition(S, N)]
+    items = np.array([[0, b[i], b[i + 1], 0, b[i + 1]] for i in range(N)], np.int64)
+    o = torch.empty((S, w["hq"], d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w["hq"], S), dtype=torch.float32, device="cuda")
+    fws = torch.empty(max(sa.segattn_fwd_workspace(sa.make_shape(q, k), items), 16), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(calls):
+        sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_us = e0.elapsed_time(e1) * 1e3 / calls
+    flops = 4 * d * visible_pairs([S]) * w["hq"]
+    print(json.dumps({"latency": "fwd", "workload": w["name"], "segments": N, "bounds": b, "calls": calls,
+                      "gpu_us_per_call": round(gpu_us, 2), "host_us_per_call": round(wall * 1e6 / calls, 2),
+                      "flops_per_call": flops, "tflops_at_gpu_time": round(flops / (gpu_us * 1e-6) / 1e12, 3)}),
+          flush=True)
+
+
 def offload_bench(torch, sa, synth, reps=5):
     """Sequence-aware offloading on the 32768-token workload (8 FLOPs-
     balanced segments).  Three per-step timings: the one-launch path, the
@@ -482,6 +523,9 @@ def main():
         return
     if args.offload:
         offload_bench(torch, sa, synth)
+        return
+    if args.latency_c1:
+        c1_latency(torch, sa, synth)
         return
     W = Workload(args.workload, torch, sa, synth)
     stream = torch.cuda.current_stream()
