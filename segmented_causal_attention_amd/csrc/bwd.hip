@@ -18,10 +18,12 @@
 //   walks every (item, query head of the group, 64-row query tile) that can
 //   see its keys, one tile per barrier.  In iteration i the dV wavefront
 //   computes S = Q K^T and P of tile i, leaves P (bf16) in an LDS buffer and
-//   accumulates dV += P^T dO; the dK wavefront works one tile behind: dP =
-//   dO V^T of tile i-1 (its accumulators start from -D, so they hold
-//   dP - D), dS = P (dP - D) with the P left in iteration i-1, and dK +=
-//   dS^T Q.  Each wavefront keeps only its own key-side operand (K or V) and
+//   accumulates dV += P^T dO.  The dK wavefront first finishes tile i-1:
+//   dS = P (dP - D) with the P left in iteration i-1 and the dP - D it
+//   computed then, and dK += dS^T Q; then it computes dP = dO V^T of tile i
+//   (its accumulators start from -D, so they hold dP - D).  The two
+//   wavefronts on a SIMD thus run their matrix products and their
+//   elementwise work at different times.  Each wavefront keeps only its own key-side operand (K or V) and
 //   accumulator in registers, so two fit on every SIMD, and the two do equal
 //   MFMA work (2 products each per tile).  Q and dO tiles are staged once, in
 //   the column layout: row reads for the products over the head dim,
@@ -278,7 +280,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   // Iteration i: stage i is published; stage i+AHEAD is copied into the slot
   // that step i-2 used (finished by both roles); the dV wavefronts work on
   // step i in slot i % NS and hand P over in buffer i % NP; the dK
-  // wavefronts work on step i-1 in slot (i-1) % NS with its P.
+  // wavefronts finish step i-1 in slot (i-1) % NS with its P, then compute
+  // dP - D of step i in slot i % NS.
   constexpr int AHEAD = NS - 2;         // stages copied ahead of the dV step
   constexpr int NP = L::kKvPBufs;       // P hand-over buffers
   constexpr int LW = 2 * Loader::kInstr;  // copies per stage (wavefront 0: + 2 rows of statistics)
@@ -300,166 +303,195 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   // 32qp + 8*lg + 0..7 for its key 16nk + l16 -- the A operand layout of the
   // contraction over query rows.  Slots are compile-time constants so every
   // LDS read is a precomputed lane offset plus an immediate.
-  auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
-    constexpr int bv = decltype(slot)::value;  // dV role: step i
-    constexpr int bk = (bv + NS - 1) % NS;     // dK role: step i-1
-    // stage i landed; the stages copied after it may stay in flight
-    if constexpr (AHEAD == 1)
-      wait_vm<0>();  // only stage i was in flight
-    else if (wave == 0)
-      wait_stages<LW + 2, 3>(issued - done - 1);
-    else
-      wait_stages<LW, 3>(issued - done - 1);
-    ring_barrier();  // stage i visible; P of step i-1 visible; slot (i+AHEAD) % NS free
-    if (ld.item >= 0) {
-      stage(ld, (bv + AHEAD) % NS);
-      ld = walk.advance(ld);
-      ++issued;
-    }
-    const KvStep st = dk_role ? pk : cp;
-    if (st.item >= 0) {
-      const int k_lo = st.k_lo, k_hi = st.k_hi, q_hi = st.q_hi;
-      const int qt0 = st.qt0;
-      const int qt1 = min(qt0 + BQ, q_hi);
-      if (has_keys && kw0 < qt1) {
-        const int b = dk_role ? bk : bv;
-        const __bf16 *Qs = lds + b * BUF, *dOs = Qs + C::TSZ;
-        const __bf16 *Xs = dk_role ? dOs : Qs;  // A rows: S = Q K^T or dP = dO V^T
-        bf16x8 opa[2][2];                       // [qp][nk]: P (dV role) or dS (dK role)
-        f32x4 xs[2][2][2];                      // [qp][ab][nk]: S or dP - D
-        // The contraction over the head dim.  The dV role starts from zero
-        // (S); the dK role from -D of the lane's rows (dP - D).  One copy
-        // per role, so neither carries the other's start values.
-        auto contract = [&](auto dkc) __attribute__((always_inline)) {
+  //
+  // Does step st have work for this wavefront's keys?
+  auto active = [&](const KvStep &st) __attribute__((always_inline)) {
+    return st.item >= 0 && has_keys && kw0 < min(st.qt0 + BQ, st.q_hi);
+  };
+  // X = (rows of Xs) x (this wavefront's keys)^T over the head dim: S = Q K^T
+  // from zero (dV role), or dP = dO V^T from -D of the rows of ring slot SL,
+  // which leaves dP - D (dK role).
+  auto rows_x = [&](const __bf16 *Xs, f32x4 (&xs)[2][2][2], auto dkc, auto slc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slc)::value;
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp)
+#pragma unroll
+      for (int ab = 0; ab < 2; ++ab) {
+        f32x4 x0 = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if constexpr (decltype(dkc)::value) x0 = *reinterpret_cast<const f32x4 *>(&stat[SL][1][32 * qp + 8 * lg + 4 * ab]);
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = x0;
+      }
+    pipelined<2 * C::KS>(
+        [&](auto ic) __attribute__((always_inline)) {
+          constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+          struct {
+            bf16x8 f[2];
+          } xa;
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
+          return xa;
+        },
+        [&](auto ic, const auto &xa) __attribute__((always_inline)) {
+          constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], xs[qp][ab][nk]);
+        });
+  };
+  // acc += opa^T Bt: dV += P^T dO or dK += dS^T Q; sub-step nt: the
+  // transposed fragments of head-dim block nt, both halves
+  auto accumulate = [&](const __bf16 *Bt, const bf16x8 (&opa)[2][2]) __attribute__((always_inline)) {
+    pipelined<C::NT>(
+        [&](auto ntc) __attribute__((always_inline)) {
+          constexpr int nt = decltype(ntc)::value;
+          struct {
+            bf16x8 f[2];
+          } bt;
+#pragma unroll
+          for (int qp = 0; qp < 2; ++qp) bt.f[qp] = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
+          return bt;
+        },
+        [&](auto ntc, const auto &bt) __attribute__((always_inline)) {
+          constexpr int nt = decltype(ntc)::value;
 #pragma unroll
           for (int qp = 0; qp < 2; ++qp)
 #pragma unroll
-            for (int ab = 0; ab < 2; ++ab) {
-              f32x4 x0 = (f32x4){0.f, 0.f, 0.f, 0.f};
-              if constexpr (decltype(dkc)::value)  // -D of rows 32qp + 8lg + 4ab + 0..3
-                x0 = *reinterpret_cast<const f32x4 *>(&stat[bk][1][32 * qp + 8 * lg + 4 * ab]);
-#pragma unroll
-              for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = x0;
-            }
-          // sub-step i = (qp, ks): the two row fragments of half qp, depth step ks
-          pipelined<2 * C::KS>(
-              [&](auto ic) __attribute__((always_inline)) {
-                constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
-                struct {
-                  bf16x8 f[2];
-                } xa;
-#pragma unroll
-                for (int ab = 0; ab < 2; ++ab) xa.f[ab] = lds_row8(Xs, roff[ks] + (32 * qp + 4 * ab) * 2 * D);
-                return xa;
-              },
-              [&](auto ic, const auto &xa) __attribute__((always_inline)) {
-                constexpr int qp = decltype(ic)::value / C::KS, ks = decltype(ic)::value % C::KS;
-#pragma unroll
-                for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-                  for (int nk = 0; nk < 2; ++nk) xs[qp][ab][nk] = mfma16(xa.f[ab], xf[nk][ks], xs[qp][ab][nk]);
-              });
-        };
-        if (dk_role)
-          contract(std::true_type{});
-        else
-          contract(std::false_type{});
-        if (!dk_role) {
-          // P = exp(S - LSE), masked on boundary tiles.  Rows past q_hi of a
-          // partial tile repeat the last row in LDS and must drop out too.
-          const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
-          // The masked variant is a separate code path so that interior
-          // tiles carry no per-element compares.
-          auto make_p = [&](auto maskc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int qp = 0; qp < 2; ++qp) {
-              // -LSE in base 2 for rows 32qp + 8lg + 0..7
-              const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[bv][0][32 * qp + 8 * lg]) * -kLog2e;
-              const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[bv][0][32 * qp + 8 * lg + 4]) * -kLog2e;
-#pragma unroll
-              for (int nk = 0; nk < 2; ++nk) {
-                // Row q = qt0 + 8lg + c (c = 32qp + 4ab + i) sees key `key` iff
-                // key - qt0 - 8lg <= c <= q_hi - 1 - qt0 - 8lg and k_lo <= key < k_hi:
-                // all of (c - c_lo), (c_hi - c) and kin are >= 0.  Their sign bit
-                // picks a +inf / -inf bound for the exponent's argument (no
-                // per-element compares, which would hold scalar register pairs).
-                const int key = kw0 + 16 * nk + l16;
-                const int c_lo = key - qt0 - 8 * lg, c_hi = q_hi - 1 - qt0 - 8 * lg;
-                const int kin = (key - k_lo) | (k_hi - 1 - key);
-                f32x4 pv[2];
-#pragma unroll
-                for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) {
-                    float arg = fmaf(xs[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]);
-                    if constexpr (decltype(maskc)::value) {
-                      const int c = 32 * qp + 4 * ab + i;
-                      const uint32_t sign = (uint32_t)((c - c_lo) | (c_hi - c) | kin) & 0x80000000u;
-                      arg = fminf(arg, __builtin_bit_cast(float, sign | 0x7f800000u));
-                    }
-                    pv[ab][i] = fast_exp2(arg);
-                  }
-                opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
-                *reinterpret_cast<bf16x8 *>(pshare[bv % NP][kgrp][qp][nk][lane]) = opa[qp][nk];
-              }
-            }
-          };
-          if (need_mask)
-            make_p(std::true_type{});
-          else
-            make_p(std::false_type{});
-        } else {
-          // dS = P (dP - D) with the P the dV wavefront left one iteration ago
-#pragma unroll
-          for (int qp = 0; qp < 2; ++qp) {
-#pragma unroll
-            for (int nk = 0; nk < 2; ++nk) {
-              const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk % NP][kgrp][qp][nk][lane]);
-              f32x4 ds[2];
-#pragma unroll
-              for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const uint32_t w = ph[2 * ab + (i >> 1)];
-                  const float p = (i & 1) ? bf16_hi(w) : bf16_lo(w);
-                  ds[ab][i] = p * xs[qp][ab][nk][i];
-                }
-              opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
-            }
-          }
-        }
-        // dV += P^T dO or dK += dS^T Q; sub-step nt: the transposed
-        // fragments of head-dim block nt, both halves
-        const __bf16 *Bt = dk_role ? Qs : dOs;
-        pipelined<C::NT>(
-            [&](auto ntc) __attribute__((always_inline)) {
-              constexpr int nt = decltype(ntc)::value;
-              struct {
-                bf16x8 f[2];
-              } bt;
-#pragma unroll
-              for (int qp = 0; qp < 2; ++qp) bt.f[qp] = lds_col8<D>(Bt, coff[nt] + 32 * qp * 2 * D);
-              return bt;
-            },
-            [&](auto ntc, const auto &bt) __attribute__((always_inline)) {
-              constexpr int nt = decltype(ntc)::value;
-#pragma unroll
-              for (int qp = 0; qp < 2; ++qp)
-#pragma unroll
-                for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt.f[qp], acc[nk][nt]);
-            });
-      }
-    }
-    pk = cp;
-    if (cp.item >= 0) {
-      cp = walk.advance(cp);
-      ++done;
-    }
-    return pk.item >= 0;
+            for (int nk = 0; nk < 2; ++nk) acc[nk][nt] = mfma16(opa[qp][nk], bt.f[qp], acc[nk][nt]);
+        });
   };
-  if (cp.item >= 0)
-    while (ring_pass<0, NS>(step)) {
+  // dV wavefronts, iteration i: S = Q K^T, P = exp(S - LSE) (masked on
+  // boundary tiles; rows past q_hi of a partial tile repeat the last row in
+  // LDS and drop out too), P handed to the dK wavefront through LDS, then
+  // dV += P^T dO -- all of step i.
+  auto dv_work = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int bslot = decltype(slot)::value;
+    if (!active(cp)) return;
+    const __bf16 *Qs = lds + bslot * BUF, *dOs = Qs + C::TSZ;
+    const int k_lo = cp.k_lo, k_hi = cp.k_hi, q_hi = cp.q_hi, qt0 = cp.qt0;
+    f32x4 xs[2][2][2];
+    rows_x(Qs, xs, std::false_type{}, slot);
+
+    bf16x8 opa[2][2];
+    const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
+    // The masked variant is a separate code path so that interior tiles
+    // carry no mask arithmetic.
+    auto make_p = [&](auto maskc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp) {
+        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&stat[bslot][0][32 * qp + 8 * lg]) * -kLog2e;
+        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&stat[bslot][0][32 * qp + 8 * lg + 4]) * -kLog2e;
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) {
+          // Row q = qt0 + 8lg + c (c = 32qp + 4ab + i) sees key `key` iff
+          // key - qt0 - 8lg <= c <= q_hi - 1 - qt0 - 8lg and k_lo <= key < k_hi:
+          // all of (c - c_lo), (c_hi - c) and kin are >= 0.  Their sign bit
+          // picks a +inf / -inf bound for the exponent's argument (no
+          // per-element compares, which would hold scalar register pairs).
+          const int key = kw0 + 16 * nk + l16;
+          const int c_lo = key - qt0 - 8 * lg, c_hi = q_hi - 1 - qt0 - 8 * lg;
+          const int kin = (key - k_lo) | (k_hi - 1 - key);
+          f32x4 pv[2];
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float arg = fmaf(xs[qp][ab][nk][i], c2, ab ? l1[i] : l0[i]);
+              if constexpr (decltype(maskc)::value) {
+                const int c = 32 * qp + 4 * ab + i;
+                const uint32_t sign = (uint32_t)((c - c_lo) | (c_hi - c) | kin) & 0x80000000u;
+                arg = fminf(arg, __builtin_bit_cast(float, sign | 0x7f800000u));
+              }
+              pv[ab][i] = fast_exp2(arg);
+            }
+          opa[qp][nk] = pack_bf16x8(pv[0], pv[1]);
+          *reinterpret_cast<bf16x8 *>(pshare[bslot % NP][kgrp][qp][nk][lane]) = opa[qp][nk];
+        }
+      }
+    };
+    if (need_mask)
+      make_p(std::true_type{});
+    else
+      make_p(std::false_type{});
+
+    accumulate(dOs, opa);
+
+  };
+  // dK wavefronts, iteration i: dS = P (dP - D) and dK += dS^T Q of step
+  // i-1 (P from the dV wavefront, dP - D kept from the previous iteration),
+  // then dP - D of step i.  In this order the dS arithmetic runs beside the
+  // dV wavefront's S products and the dK products beside its exponentials,
+  // so the two wavefronts sharing a SIMD tend to keep its matrix unit busy
+  // in turn.
+  f32x4 dp[2][2][2];  // dP - D of the step the dV wavefronts just did
+  auto dk_work = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int bv = decltype(slot)::value;
+    constexpr int bk = (bv + NS - 1) % NS;
+    if (active(pk)) {
+      bf16x8 opa[2][2];
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp)
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) {
+          const u32x4 ph = *reinterpret_cast<const u32x4 *>(pshare[bk % NP][kgrp][qp][nk][lane]);
+          f32x4 ds[2];
+#pragma unroll
+          for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t w = ph[2 * ab + (i >> 1)];
+              const float pp = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+              ds[ab][i] = pp * dp[qp][ab][nk][i];
+            }
+          opa[qp][nk] = pack_bf16x8(ds[0], ds[1]);
+        }
+
+      accumulate(lds + bk * BUF, opa);
+
     }
+    if (active(cp)) {
+      rows_x(lds + bv * BUF + C::TSZ, dp, std::true_type{}, slot);
+
+    }
+  };
+  // The ring, one copy per role (same walkers, so the same barriers).
+  auto ring = [&](auto &work) __attribute__((always_inline)) {
+    auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
+      constexpr int bv = decltype(slot)::value;  // step i (dV role)
+      // stage i landed; the stages copied after it may stay in flight
+      if constexpr (AHEAD == 1)
+        wait_vm<0>();  // only stage i was in flight
+      else if (wave == 0)
+        wait_stages<LW + 2, 3>(issued - done - 1);
+      else
+        wait_stages<LW, 3>(issued - done - 1);
+      ring_barrier();
+
+      if (ld.item >= 0) {
+        stage(ld, (bv + AHEAD) % NS);
+        ld = walk.advance(ld);
+        ++issued;
+      }
+
+      work(slot);
+      pk = cp;
+      if (cp.item >= 0) {
+        cp = walk.advance(cp);
+        ++done;
+      }
+
+
+      return pk.item >= 0;
+    };
+    if (cp.item >= 0)
+      while (ring_pass<0, NS>(step)) {
+      }
+  };
+  if (dk_role)
+    ring(dk_work);
+  else
+    ring(dv_work);
 
   // ---- epilogue: lane holds rows key = kw0 + 16nk + 4lg + i, column 16nt + l16
   GT *outg = static_cast<GT *>(dk_role ? a.dk : a.dv);
