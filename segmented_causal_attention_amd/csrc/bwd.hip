@@ -291,6 +291,18 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
   KvStep pk{-1, 0, 0, 0, 0, 0, 0, 0, 0};
   KvStep ld = cp;
   int issued = 0, done = 0;  // stages copied / steps of the dV wavefronts started
+  // The copies of the next stage are issued after each wavefront's first
+  // products of the step (or at its end when it has none) rather than right
+  // after the barrier, where all eight wavefronts would queue theirs at once.
+  bool pend = false;
+  auto stage_if = [&](auto sc) __attribute__((always_inline)) {
+    if (pend) {
+      stage(ld, decltype(sc)::value);
+      ld = walk.advance(ld);
+      ++issued;
+      pend = false;
+    }
+  };
 #pragma unroll
   for (int s = 0; s < AHEAD; ++s)
     if (ld.item >= 0) {
@@ -372,6 +384,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
     const int k_lo = cp.k_lo, k_hi = cp.k_hi, q_hi = cp.q_hi, qt0 = cp.qt0;
     f32x4 xs[2][2][2];
     rows_x(Qs, xs, std::false_type{}, slot);
+    stage_if(std::integral_constant<int, (bslot + AHEAD) % NS>{});
 
     bf16x8 opa[2][2];
     const bool need_mask = !(kw0 + 31 <= qt0 && kw0 >= k_lo && kw0 + 32 <= k_hi && qt0 + BQ <= q_hi);
@@ -448,6 +461,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
         }
 
       accumulate(lds + bk * BUF, opa);
+      stage_if(std::integral_constant<int, (bv + AHEAD) % NS>{});
 
     }
     if (active(cp)) {
@@ -468,13 +482,9 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs &a, int x, char *smem) {
         wait_stages<LW, 3>(issued - done - 1);
       ring_barrier();
 
-      if (ld.item >= 0) {
-        stage(ld, (bv + AHEAD) % NS);
-        ld = walk.advance(ld);
-        ++issued;
-      }
-
+      pend = ld.item >= 0;
       work(slot);
+      stage_if(std::integral_constant<int, (bv + AHEAD) % NS>{});
       pk = cp;
       if (cp.item >= 0) {
         cp = walk.advance(cp);
@@ -646,11 +656,17 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
     constexpr int buf = decltype(slot)::value;
     wait_stages<2 * Loader::kInstr, NS>(issued - done - 1);
     ring_barrier();  // stage `buf` visible; the slot staged next is free
-    if (ld.item >= 0) {
-      stage(ld, (buf + NS - 1) % NS);
-      ld = walk.advance(ld);
-      ++issued;
-    }
+    // copies of the next stage: after the first key pair's products (or at
+    // the end of a step without rows), not all at once after the barrier
+    bool pend = ld.item >= 0;
+    auto stage_if = [&]() __attribute__((always_inline)) {
+      if (pend) {
+        stage(ld, (buf + NS - 1) % NS);
+        ld = walk.advance(ld);
+        ++issued;
+        pend = false;
+      }
+    };
     const int kv0 = cp.kv0;
     const int k_hi = cp.k_hi;
     if (has_rows && kv0 <= rw_end - 1) {
@@ -695,6 +711,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
                   dp[nq][ab] = mfma16(f.v[ab], dof[nq][ks], dp[nq][ab]);
                 }
             });
+        if (kp == 0) stage_if();
         // dS = P (dP - D); the masked variant is a separate code path so
         // that interior tiles carry no per-element compares.
         auto make_ds = [&](auto maskc) __attribute__((always_inline)) {
@@ -746,6 +763,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
               for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka.f[kp], dsb[nq][kp], dq[nq][nt]);
           });
     }
+    stage_if();
     cp = walk.advance(cp);
     ++done;
     return cp.item >= 0;
