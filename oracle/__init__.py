@@ -16,6 +16,9 @@ attention  -- causal softmax attention forward / backward in float64, the
               "segmented + merged == unsegmented".
 offload    -- the sequence-aware offload plan (ratios alpha_i and the GPU
               memory recurrence) in float64.
+chunking   -- workload-balanced chunking of a variable-length batch (mesh
+              from the longest sequence, mesh cuts, best-fit-decreasing
+              packing of tails and short sequences) in float64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, library routines, finite differences and exact
@@ -44,3 +47,4 @@ from .attention import (  # noqa: F401
     attention_keys_bwd,
 )
 from .offload import plan_offload, offload_rows  # noqa: F401,E402
+from .chunking import chunk, chunk_items  # noqa: F401,E402
