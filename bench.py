@@ -5,12 +5,18 @@
     python bench.py --sweep-segments
     python bench.py --offload
     python bench.py --latency-c1
+    python bench.py --chunking
 
 --sweep-segments times the same fwd+bwd path on 131072 tokens (32 heads,
 d = 128, bf16) cut into N equal-length segments, N = 1, 2, 4, ..., 1024, each
 segment's queries attending to the whole resident prefix: the segment-length
 sweep of SPPO section 4 (Figure 7) on this GPU.  It prints one JSON line per
 N instead of the single benchmark line.
+
+--chunking plans the varlen batch with workload-balanced chunking
+(InfiniPipe section III-B, Algorithm 1) after fitting eq. (1)'s cost to this
+GPU, and times it chunk by chunk (one JSON line for the fit, then one per
+plan).
 
 --latency-c1 times the small oracle-identity case (1024 tokens, one head,
 d = 64, fp32 inputs, 4 FLOPs-balanced segments, forward only), which is
@@ -104,6 +110,8 @@ def parse():
                    help="per-call latency of the 1024-token, 1-head, d=64 fp32 forward (one line)")
     p.add_argument("--offload", action="store_true",
                    help="per-segment fwd/bwd with Q/O/LSE offloaded to host memory and prefetched (one line)")
+    p.add_argument("--chunking", action="store_true",
+                   help="workload-balanced chunking of the varlen batch: cost fit, then per-chunk timing per K")
     p.add_argument("--sweep-segments", action="store_true",
                    help="time fwd+bwd over 131072 tokens in N = 1..1024 equal segments (one line per N)")
     return p.parse_args()
@@ -340,6 +348,80 @@ def segment_sweep(torch, sa, synth, max_segments=1024, warmup=1, steps=3):
         N *= 2
 
 
+def chunking_bench(torch, sa, synth, reps=3, token_cap=16384, ks=(1, 2, 3, 4, 5)):
+    """Workload-balanced chunking (InfiniPipe section III-B, Algorithm 1) of
+    the 262144-token varlen batch (32 query / 8 KV heads, d = 128).  First the
+    slice cost of eq. (1), t(L) = alpha1 L^2 + alpha2 L + beta, is fitted to
+    this GPU's fwd+bwd launch times of single sequences of 1K..32K tokens
+    (the D reduction over all rows, once per schedule, left out); then for
+    each K the chunks are planned with the fitted alpha1, alpha2 and a token
+    capacity of 16384 tokens, and run as one forward launch per chunk, one D
+    reduction, and one backward launch per chunk in reverse order (fp32
+    gradients accumulating across launches).  Reported per plan: chunk count,
+    per-chunk fwd+bwd time max / mean (the balance the algorithm aims at),
+    total time and TFLOP/s.  The slicing rule of the main benchmark (16384-
+    token FLOPs-balanced slices) runs the same way with each item as a chunk."""
+    W = Workload("c4", torch, sa, synth)
+    q, k, v, do, hq, d, T = W.q, W.k, W.v, W.do, W.hq, W.d, W.T
+    shape = sa.make_shape(q, k)
+    o = torch.empty((T, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+    g = [torch.zeros(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v)]
+    E = torch.cuda.Event
+
+    def run_chunks(chunks):
+        allitems = np.concatenate(chunks)
+        fws = torch.empty(max(sa.segattn_fwd_workspace(shape, allitems), 16), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(sa.segattn_bwd_workspace(shape, allitems), dtype=torch.uint8, device="cuda")
+        per, tot = [], []
+        for it in range(1 + reps):
+            for x in g:
+                x.zero_()
+            ev = [[E(enable_timing=True) for _ in range(4)] for _ in chunks]
+            for c, ch in enumerate(chunks):
+                ev[c][0].record()
+                sa.segattn_fwd(q, k, v, ch, o=o, lse=lse, workspace=fws)
+                ev[c][1].record()
+            sa.segattn_bwd_preprocess(q, k, o, do, allitems, bws)
+            for c in reversed(range(len(chunks))):
+                ev[c][2].record()
+                sa.segattn_bwd(q, k, v, o, lse, do, chunks[c][::-1].copy(), dq=g[0], dk=g[1], dv=g[2],
+                               accumulate=True, d_ready=True, workspace=bws)
+                ev[c][3].record()
+            torch.cuda.synchronize()
+            if it:
+                per.append([e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev])
+                tot.append(ev[0][0].elapsed_time(ev[0][3]))
+        return np.median(np.array(per), axis=0), float(np.median(tot))
+
+    flops = W.flops_fwd + W.flops_bwd
+    # eq. (1) fitted on this GPU: single sequences at the start of the batch
+    Ls = [1024, 2048, 4096, 8192, 16384, 32768]
+    ts = [float(run_chunks([np.array([[0, 0, L, 0, L]], np.int64)])[0][0]) for L in Ls]  # fwd + bwd launches
+    A = np.array([[L * L, L, 1.0] for L in Ls], np.float64)
+    (a1, a2, beta), *_ = np.linalg.lstsq(A, np.array(ts), rcond=None)
+    a2 = max(float(a2), 0.0)  # eq. (1)'s linear term is not negative
+    print(json.dumps({"chunking": "cost_fit", "workload": "varlen262144_Hq32_Hkv8_d128_bf16",
+                      "lengths": Ls, "fwd_bwd_ms": [round(t, 4) for t in ts],
+                      "alpha1_ms_per_tok2": float(a1), "alpha2_ms_per_tok": a2, "beta_ms": float(beta)}),
+          flush=True)
+
+    def report(kind, chunks, extra):
+        per, tot = run_chunks(chunks)
+        print(json.dumps({"chunking": kind, **extra, "chunks": len(chunks),
+                          "items": int(sum(len(c) for c in chunks)),
+                          "chunk_ms_max": round(float(per.max()), 3), "chunk_ms_mean": round(float(per.mean()), 3),
+                          "chunk_ms_min": round(float(per.min()), 3),
+                          "imbalance_max_over_mean": round(float(per.max() / per.mean()), 3),
+                          "total_ms": round(tot, 3), "tflops": round(flops / (tot * 1e-3) / 1e12, 1)}), flush=True)
+
+    report("slices_16384_one_item_per_chunk", [it[None, :] for it in W.items], {"token_cap": 16384})
+    for K in ks:
+        items, owner, nch, tt = sa.segattn_chunk_varlen(W.cu, K, float(a1), a2, token_cap)
+        report("workload_balanced", [items[owner == c] for c in range(nch)],
+               {"K": K, "token_cap": token_cap, "final_time_threshold": tt})
+
+
 def c1_latency(torch, sa, synth, calls=500, warmup=50):
     """Per-call latency of the forward over the 1024-token, one-head, d = 64
     fp32 workload in 4 FLOPs-balanced segments (one segattn_fwd call with 4
@@ -526,6 +608,9 @@ def main():
         return
     if args.latency_c1:
         c1_latency(torch, sa, synth)
+        return
+    if args.chunking:
+        chunking_bench(torch, sa, synth)
         return
     W = Workload(args.workload, torch, sa, synth)
     stream = torch.cuda.current_stream()

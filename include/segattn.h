@@ -122,6 +122,38 @@ int segattn_partition_varlen(const int64_t *cu_seqlens, int32_t nseq, int64_t ma
 int segattn_ring_items(const int64_t *bounds, int32_t N, int64_t block,
                        segattn_item *items, int32_t cap, int32_t *n_items);
 
+/* Workload-balanced chunks of a packed variable-length batch (InfiniPipe
+ * section III-B, Algorithm 1; slice cost of section III-A2, eq. (1)).  A
+ * slice of s tokens after a context of C tokens costs
+ * alpha1 ((C + s)^2 - C^2) + alpha2 s.
+ *  1. The longest sequence L is cut into min(K, L) slices of equal cost (the
+ *     mesh): inner boundary i is the integer b minimising |K f(b) - i f(L)|,
+ *     f(b) = alpha1 b^2 + alpha2 b, ties to the smaller b.
+ *  2. Every sequence is cut at the inner mesh boundaries inside it; the
+ *     pieces before its last cut are split chunks, the last piece its tail
+ *     slice.  A sequence without a cut is short; empty ones are dropped.
+ *  3. Best-fit-decreasing: one bucket per tail slice, ordered by
+ *     time / tokens ascending (ties: older bucket first); short sequences
+ *     by decreasing cost (ties: earlier sequence first).  A sequence opens a
+ *     new bucket when even the bucket with the fewest tokens would exceed
+ *     token_cap (T_m); otherwise it joins the first bucket within both the
+ *     time threshold T_t (initially f(L) / min(K, L)) and T_m; if none,
+ *     T_t becomes the least bucket time plus the sequence's cost over the
+ *     buckets within T_m, and the placement is retried.
+ * Output: the split chunks (by sequence, then position), then the buckets in
+ * the order they were opened, as work items {seq_off = cu[j], q = [lo, hi),
+ * k = [0, hi)} grouped by chunk; chunk_of[i] (optional, may be NULL) is the
+ * chunk of item i.  *n_chunks receives the chunk count and *time_threshold
+ * (optional) the final T_t.  All float64 arithmetic in a fixed order.
+ * cu_seqlens: HOST int64[nseq + 1] from 0, non-decreasing, <= 2^31-1 tokens.
+ * Errors: E_INVALID (NULL, nseq < 1, K < 1, alpha1 <= 0, alpha2 < 0 or not
+ * finite, token_cap < 1, cu_seqlens invalid, every sequence empty),
+ * E_RANGE (> 2^31-1 tokens), E_CAPACITY (*n_items receives the size needed;
+ * nothing else is written). */
+int segattn_chunk_varlen(const int64_t *cu_seqlens, int32_t nseq, int32_t K, double alpha1, double alpha2,
+                         int64_t token_cap, segattn_item *items, int32_t *chunk_of, int32_t cap,
+                         int32_t *n_items, int32_t *n_chunks, double *time_threshold);
+
 /* ---------------------------------------------------------------- forward */
 
 /* Workspace bytes segattn_fwd needs for this shape and item table. */

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     segattn_bwd,
     segattn_bwd_preprocess,
     segattn_bwd_workspace,
+    segattn_chunk_varlen,
     segattn_copy_rows,
     segattn_fwd,
     segattn_fwd_workspace,

@@ -34,6 +34,7 @@ EXPORTS = (
     "segattn_partition",
     "segattn_partition_varlen",
     "segattn_ring_items",
+    "segattn_chunk_varlen",
     "segattn_fwd_workspace",
     "segattn_fwd",
     "segattn_merge",
@@ -85,6 +86,8 @@ def lib():
     L.segattn_partition.argtypes = [i64, i32, P(i64)]
     L.segattn_partition_varlen.argtypes = [P(i64), i32, i64, P(Item), i32, P(i32)]
     L.segattn_ring_items.argtypes = [P(i64), i32, i64, P(Item), i32, P(i32)]
+    L.segattn_chunk_varlen.argtypes = [P(i64), i32, i32, ctypes.c_double, ctypes.c_double, i64, P(Item), P(i32),
+                                       i32, P(i32), P(i32), P(ctypes.c_double)]
     L.segattn_fwd_workspace.argtypes = [P(Shape), P(Item), i32, P(sz)]
     L.segattn_fwd.argtypes = [P(Shape), vp, vp, vp, P(Item), i32, vp, i32, vp, ctypes.c_uint32, vp, sz, vp]
     L.segattn_merge.argtypes = [i64, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp]

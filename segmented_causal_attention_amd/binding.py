@@ -93,6 +93,25 @@ def segattn_partition_varlen(cu_seqlens, max_slice):
     return out
 
 
+def segattn_chunk_varlen(cu_seqlens, K, alpha1, alpha2, token_cap):
+    """Workload-balanced chunks of a packed batch: returns (items int64
+    [n, 5], chunk index of each item int32 [n], number of chunks, final time
+    threshold)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n, nc, tt = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_double(0.0)
+    L = lib()
+    args = (cu.ctypes.data_as(_I64P), len(cu) - 1, int(K), float(alpha1), float(alpha2), int(token_cap))
+    st = L.segattn_chunk_varlen(*args, None, None, 0, ctypes.byref(n), ctypes.byref(nc), ctypes.byref(tt))
+    if st != _lib.SEGATTN_E_CAPACITY:
+        check(st)
+    out = np.zeros((n.value, 5), dtype=np.int64)
+    owner = np.zeros(n.value, dtype=np.int32)
+    check(L.segattn_chunk_varlen(*args, out.ctypes.data_as(_ITEMP),
+                                 owner.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n),
+                                 ctypes.byref(nc), ctypes.byref(tt)))
+    return out, owner, nc.value, tt.value
+
+
 def segattn_ring_items(bounds, block):
     b = np.ascontiguousarray(np.asarray(bounds, dtype=np.int64))
     n = ctypes.c_int32(0)
