@@ -202,9 +202,11 @@ int segattn_bwd_workspace(const segattn_shape *shape, const segattn_item *items,
                           size_t *bytes);
 
 /* D_q = <dO_q, O_q> for every query row of the items, stored NEGATED (-D_q)
- * into the workspace (float [hq][tokens] at its start).  Lets the caller time or schedule the
- * reduction apart from the main backward kernel; segattn_bwd then takes
- * SEGATTN_D_READY.  Arguments as in segattn_bwd. */
+ * into the workspace (float [hq][tokens] at its start; entries of rows
+ * outside the items' query ranges are not written), followed by the plan
+ * tables.  Lets the caller time or schedule the reduction apart from the
+ * main backward kernel; segattn_bwd then takes SEGATTN_D_READY with items
+ * whose query rows are among these.  Arguments as in segattn_bwd. */
 int segattn_bwd_preprocess(const segattn_shape *shape, const void *o, int32_t o_dtype, const void *d_o,
                            const segattn_item *items, int32_t n_items, void *workspace, size_t ws_bytes,
                            void *stream);

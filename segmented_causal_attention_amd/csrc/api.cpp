@@ -223,6 +223,35 @@ size_t bwd_ws_bytes(const segattn_shape *s, const BwdPlan &p) {
   return bwd_delta_bytes(s) + align_up(p.items.size() * 4) + align_up(p.kvg.size() * 4) + align_up(p.qg.size() * 4);
 }
 
+// Device copies of the plan tables, after D in the workspace.
+struct BwdTables {
+  int32_t *items, *kvg, *qg;
+};
+
+// Places the three tables in the workspace and uploads them (one
+// stream-ordered upload; they are contiguous).
+hipError_t upload_bwd_tables(const segattn_shape *shape, const BwdPlan &plan, void *workspace, hipStream_t s,
+                             BwdTables &t) {
+  char *ws = static_cast<char *>(workspace);
+  size_t off = bwd_delta_bytes(shape);
+  t.items = reinterpret_cast<int32_t *>(ws + off);
+  off += align_up(plan.items.size() * 4);
+  t.kvg = reinterpret_cast<int32_t *>(ws + off);
+  off += align_up(plan.kvg.size() * 4);
+  t.qg = reinterpret_cast<int32_t *>(ws + off);
+  std::vector<int32_t> words((size_t)(t.qg - t.items) + plan.qg.size(), 0);
+  std::copy(plan.items.begin(), plan.items.end(), words.begin());
+  std::copy(plan.kvg.begin(), plan.kvg.end(), words.begin() + (t.kvg - t.items));
+  std::copy(plan.qg.begin(), plan.qg.end(), words.begin() + (t.qg - t.items));
+  return launch_upload(t.items, words.data(), (int64_t)words.size(), s);
+}
+
+PreArgs pre_args(const segattn_shape *shape, const BwdPlan &plan, const void *o, const void *d_o, float *delta,
+                 const BwdTables &t) {
+  return PreArgs{o, d_o, delta, t.items, t.qg, (int32_t)(plan.qg.size() / 4), plan.n_q_units, shape->tokens,
+                 shape->hq};
+}
+
 }  // namespace
 
 // ================================================================== forward
@@ -339,9 +368,11 @@ extern "C" int segattn_bwd_preprocess(const segattn_shape *shape, const void *o,
   if (!workspace || ws_bytes < need)
     return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
-  PreArgs a{o, d_o, static_cast<float *>(workspace), shape->tokens, shape->hq};
-  if (hipError_t e = launch_bwd_pre(a, shape->d, o_dtype, shape->in_dtype, static_cast<hipStream_t>(stream)))
-    return device_error(e, fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdTables t;
+  if (hipError_t e = upload_bwd_tables(shape, plan, workspace, s, t)) return device_error(e, fn);
+  const PreArgs a = pre_args(shape, plan, o, d_o, static_cast<float *>(workspace), t);
+  if (hipError_t e = launch_bwd_pre(a, shape->d, o_dtype, shape->in_dtype, s)) return device_error(e, fn);
   return SEGATTN_OK;
 }
 
@@ -373,27 +404,14 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   if (kv_pad + (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(workspace);
-  float *delta = reinterpret_cast<float *>(ws);
-  size_t off = bwd_delta_bytes(shape);
-  int32_t *d_items = reinterpret_cast<int32_t *>(ws + off);
-  off += align_up(plan.items.size() * 4);
-  int32_t *d_kvg = reinterpret_cast<int32_t *>(ws + off);
-  off += align_up(plan.kvg.size() * 4);
-  int32_t *d_qg = reinterpret_cast<int32_t *>(ws + off);
-
+  float *delta = static_cast<float *>(workspace);
+  BwdTables t;
+  if (hipError_t e = upload_bwd_tables(shape, plan, workspace, s, t)) return device_error(e, fn);
   if (!(flags & SEGATTN_D_READY)) {
-    PreArgs pa{o, d_o, delta, shape->tokens, shape->hq};
+    const PreArgs pa = pre_args(shape, plan, o, d_o, delta, t);
     if (hipError_t e = launch_bwd_pre(pa, shape->d, o_dtype, shape->in_dtype, s)) return device_error(e, fn);
   }
-  {
-    // the three tables are contiguous in the workspace: one upload
-    std::vector<int32_t> words((size_t)((char *)d_qg - (char *)d_items) / 4 + plan.qg.size(), 0);
-    std::copy(plan.items.begin(), plan.items.end(), words.begin());
-    std::copy(plan.kvg.begin(), plan.kvg.end(), words.begin() + (d_kvg - d_items));
-    std::copy(plan.qg.begin(), plan.qg.end(), words.begin() + (d_qg - d_items));
-    if (hipError_t e = launch_upload(d_items, words.data(), (int64_t)words.size(), s)) return device_error(e, fn);
-  }
+  int32_t *d_items = t.items, *d_kvg = t.kvg, *d_qg = t.qg;
 
   BwdArgs a;
   a.q = q;

@@ -55,11 +55,15 @@ struct FwdArgs {
   int32_t merge;         // 1: merge into the fp32 (O, LSE) already in o/lse
 };
 
-// delta[h][t] = -D = -<dO[t,h,:], O[t,h,:]> for every token row (negated: the
-// backward's products dP = dO V^T start from it and yield dP - D directly).
+// delta[h][t] = -D = -<dO[t,h,:], O[t,h,:]> for the query rows of the items
+// (negated: the backward's products dP = dO V^T start from it and yield
+// dP - D directly).  One workgroup per (q unit, query head), the q units of
+// the backward's q groups (BwdArgs below).
 struct PreArgs {
   const void *o, *d_o;
   float *delta;
+  const int32_t *items, *qg;
+  int32_t n_qg, n_q_units;
   int64_t tokens;
   int32_t hq;
 };

@@ -95,19 +95,31 @@ __global__ __launch_bounds__(256) void merge_kernel_any(MergeArgs a) {
 }
 
 // ------------------------------------------------------------- D = <dO, O>
-// One 8-element chunk per thread, d/8 threads per (token, head) row reduced
-// with xor shuffles inside the wavefront.
+// Rows [r0, r1) of one q unit of the items' q groups, one query head: d/8
+// threads per row, one 8-element chunk each, reduced with xor shuffles
+// inside the wavefront.
 template <int D, typename OT, typename GT>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
-  constexpr int CPR = D / 8;  // chunks per row: 16 or 8
-  const int64_t rows = a.tokens * a.hq;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  constexpr int CPR = D / 8;      // chunks per row: 16 or 8
+  constexpr int RPP = 256 / CPR;  // rows per pass
+  const int x = blockIdx.x, rank = x / a.hq, h = x - rank * a.hq;
+  int lo = 0, hi = a.n_qg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qg[mid * 4 + 2] <= rank)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int32_t *grp = a.qg + lo * 4;
+  const int32_t *it = a.items + grp[0] * kItemWords;
+  const int seq_off = it[0], q_lo = it[1], q_hi = it[2];
+  const int r1 = q_hi - (rank - grp[2]) * kBwdQBM, r0 = max(q_lo, r1 - kBwdQBM);
+  const int c = threadIdx.x % CPR;
   const OT *og = static_cast<const OT *>(a.o);
   const GT *dg = static_cast<const GT *>(a.d_o);
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < rows * CPR; idx += stride) {
-    const int64_t row = idx / CPR;  // row = t * hq + h
-    const int c = (int)(idx - row * CPR);
-    float acc = 0.f;
+  for (int r = r0 + (int)threadIdx.x / CPR; r < r1; r += RPP) {
+    const int64_t row = ((int64_t)seq_off + r) * a.hq + h;
     const OT *op = og + row * D + 8 * c;
     const GT *gp = dg + row * D + 8 * c;
     float ov[8], gv[8];
@@ -125,15 +137,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
       const u32x4 w = *reinterpret_cast<const u32x4 *>(gp);
       for (int i = 0; i < 4; ++i) { gv[2 * i] = bf16_lo(w[i]); gv[2 * i + 1] = bf16_hi(w[i]); }
     }
+    float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf(ov[i], gv[i], acc);
 #pragma unroll
     for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (c == 0) {
-      const int64_t t = row / a.hq;
-      const int h = (int)(row - t * a.hq);
-      a.delta[(int64_t)h * a.tokens + t] = -acc;  // stored negated: the backward's start value of dP
-    }
+    if (c == 0) a.delta[(int64_t)h * a.tokens + seq_off + r] = -acc;  // negated: the start value of dP
   }
 }
 
@@ -174,8 +183,7 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
 
 hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s) {
   using namespace dev;
-  const int64_t work = a.tokens * a.hq * (d / 8);
-  const dim3 grid(grid_for(work, 256)), block(256);
+  const dim3 grid((unsigned)((int64_t)a.n_q_units * a.hq)), block(256);
   const bool ob = o_dtype == 0, gb = in_dtype == 0;
 #define SEGATTN_PRE(DD, OT, GT) hipLaunchKernelGGL((bwd_pre_kernel<DD, OT, GT>), grid, block, 0, s, a)
   if (d == 128) {

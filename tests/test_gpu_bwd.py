@@ -132,6 +132,25 @@ def test_preprocess_then_d_ready():
         assert torch.equal(a, b)
 
 
+def test_preprocess_writes_only_item_rows():
+    """D is reduced over the query rows of the items only (a per-segment
+    backward call costs its own rows, not the whole batch's)."""
+    T, hq, d = 700, 2, 128
+    say(f"case bwd D rows T={T}")
+    q, k, v, do = _inputs(30, T, hq, hq, d)
+    items = np.array([[0, 200, 450, 0, 450]], np.int64)
+    o, lse = sa.segattn_fwd(q, k, v, items, o_dtype=torch.bfloat16)
+    shape = sa.make_shape(q, k)
+    ws = torch.empty(sa.segattn_bwd_workspace(shape, items), dtype=torch.uint8, device=DEV)
+    delta = ws[: hq * T * 4].view(torch.float32).view(hq, T)
+    delta.fill_(7.0)
+    sa.segattn_bwd_preprocess(q, k, o, do, items, ws)
+    want = -(o.float() * do.float()).sum(-1).transpose(0, 1)
+    torch.cuda.synchronize()
+    assert bool((delta[:, :200] == 7.0).all()) and bool((delta[:, 450:] == 7.0).all())
+    np.testing.assert_allclose(host64(delta[:, 200:450]), host64(want[:, 200:450]), rtol=1e-4, atol=1e-4)
+
+
 def test_repeat_run_is_bitwise_identical():
     T, hq, d = 900, 4, 128
     say(f"case bwd determinism T={T}")
