@@ -12,13 +12,13 @@ What the pages fix, and the readings taken where they are silent:
   The factor 1/N and the per-chunk constant beta1/d_p are common to every
   chunk on one device and are left out.  (C + s)^2 - C^2 = s(2C + s) is
   formed exactly in integers, then scaled in float64.
-* Mesh (line 1).  The longest sequence L is cut into K slices of equal
+* Mesh.  The longest sequence L is cut into K slices of equal
   time: boundary b_i is the integer minimising |K f(b) - i f(L)| with
   f(b) = alpha1 b^2 + alpha2 b (ties to the smaller b), found from the
   positive root of K f(b) = i f(L) and a check of its integer neighbours.
   With alpha1 = alpha2 = 1/2, f(b) = b(b+1)/2 and the mesh is the
   FLOPs-balanced segment partition.
-* Split (line 2).  A sequence is cut at every inner mesh boundary that lies
+* Split.  A sequence is cut at every inner mesh boundary that lies
   strictly inside it; the pieces before the last cut are split chunks (one
   slice each, its context the tokens before it), the last piece is its tail
   slice.  A sequence no mesh boundary falls inside is a short sequence.
@@ -29,7 +29,7 @@ What the pages fix, and the readings taken where they are silent:
   capacity per bucket.  A bucket's token count is the sum of its slices
   (a tail's context is not in it: those keys and values belong to the
   split chunks).
-* Buckets (lines 3-28).  One bucket per tail slice, kept ordered by
+* Buckets.  One bucket per tail slice, kept ordered by
   tot_time / tot_tokens ascending (ties: the older bucket first); short
   sequences taken longest-time first (ties: earlier sequence first).  A
   short sequence opens a new bucket when even the bucket with the fewest
@@ -39,7 +39,7 @@ What the pages fix, and the readings taken where they are silent:
   retried.  Reading: the least is taken over the buckets that meet T_m --
   over all buckets, as printed, the retry can repeat forever when the
   bucket with the least time is the one over T_m.
-* Output (lines 30-31).  Split chunks (by sequence, then position), then
+* Output.  Split chunks (by sequence, then position), then
   the buckets in the order they were opened: a bucket holding a tail slice
   is a hybrid chunk, the others batched chunks; members in the order they
   joined.
@@ -87,7 +87,7 @@ def mesh(L: int, K: int, alpha1: float, alpha2: float) -> list[int]:
 
 
 def split(lengths, bounds):
-    """Line 2: cut every sequence by the mesh.  Returns (split_chunks,
+    """Cut every sequence by the mesh.  Returns (split_chunks,
     tails, shorts): split chunks and tails as (sequence, context, length),
     shorts as (sequence, length); empty sequences are dropped."""
     inner = bounds[1:-1]
@@ -125,7 +125,7 @@ def chunk(lengths, K: int, alpha1: float, alpha2: float, token_cap: int):
     t_m = token_cap
     split_chunks, tails, shorts = split(lengths, bounds)
 
-    # buckets: [metric, id, tot_time, tot_tokens, members, has_tail]
+    # buckets: dicts of id (opening order), time, tokens, members, tail
     buckets = []
     for j, c, s in tails:
         t = piece_time(c, s, alpha1, alpha2)

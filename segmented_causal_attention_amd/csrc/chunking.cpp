@@ -117,13 +117,13 @@ extern "C" int segattn_chunk_varlen(const int64_t *cu, int32_t nseq, int32_t K, 
   if (cu[nseq] > kMaxTokens) return fail(SEGATTN_E_RANGE, "%s: %lld tokens > 2^31-1", fn, (long long)cu[nseq]);
   if (L == 0) return fail(SEGATTN_E_INVALID, "%s: every sequence is empty", fn);
 
-  // Line 1: mesh and thresholds.
+  // The mesh and the thresholds.
   const int32_t Km = (int32_t)std::min<int64_t>(K, L);
   const std::vector<int64_t> mesh = make_mesh(L, Km, alpha1, alpha2);
   double t_t = mesh_f(L, alpha1, alpha2) / (double)Km;
   const int64_t t_m = token_cap;
 
-  // Line 2: cut every sequence by the inner mesh boundaries inside it.
+  // Cut every sequence by the inner mesh boundaries inside it.
   std::vector<Piece> split_chunks, tails, shorts;
   for (int32_t s = 0; s < nseq; ++s) {
     const int64_t len = cu[s + 1] - cu[s];
@@ -140,7 +140,7 @@ extern "C" int segattn_chunk_varlen(const int64_t *cu, int32_t nseq, int32_t K, 
     else shorts.push_back({s, 0, len});
   }
 
-  // Lines 3-28: best-fit-decreasing packing.
+  // Best-fit-decreasing packing.
   std::vector<Bucket> buckets;
   for (const Piece &p : tails)
     buckets.push_back({(int32_t)buckets.size(), piece_time(p.ctx, p.len, alpha1, alpha2), p.len, true, {p}});
@@ -185,7 +185,7 @@ extern "C" int segattn_chunk_varlen(const int64_t *cu, int32_t nseq, int32_t K, 
       }
       if (placed) break;
       // Loosen T_t to the least time the sequence could join at, over the
-      // buckets within T_m (line 9 guarantees there is one).
+      // buckets within T_m (the check above guarantees there is one).
       bool first = true;
       for (const Bucket &b : buckets)
         if (b.tokens + n <= t_m) {
@@ -196,7 +196,7 @@ extern "C" int segattn_chunk_varlen(const int64_t *cu, int32_t nseq, int32_t K, 
     }
   }
 
-  // Lines 30-31: items of the split chunks, then of the buckets.
+  // Items of the split chunks, then of the buckets.
   int64_t needed = (int64_t)split_chunks.size();
   for (const Bucket &b : buckets) needed += (int64_t)b.members.size();
   const int64_t nch = (int64_t)split_chunks.size() + (int64_t)buckets.size();
