@@ -1,6 +1,6 @@
 """Benchmark of the segmented causal attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4tail|c5] [--no-cpu-baseline]
                     [--no-hbm-kernels]
     python bench.py --sweep-segments
     python bench.py --offload
@@ -100,7 +100,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4tail", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-hbm-kernels", action="store_true",
                    help="skip the separate merge / D-reduction bandwidth measurements")
@@ -125,7 +125,15 @@ class Workload:
     """Inputs, items and preallocated outputs of one benchmark workload."""
 
     def __init__(self, name, torch, sa, synth):
-        w = synth.WORKLOADS[name]
+        if name == "c4tail":
+            # the varlen batch at its tail seed: the least seed >= 1004 whose
+            # draw holds a sequence of 64K-128K tokens
+            seed = synth.tail_seed()
+            w = dict(synth.WORKLOADS["c4"], seed=seed)
+            w["name"] = f"{w['name']}_seed{seed}"
+            name = "c4"
+        else:
+            w = synth.WORKLOADS[name]
         self.name, self.w = name, w
         self.hq, self.hkv, self.d = w["hq"], w["hkv"], w["d"]
         if name == "c4":
