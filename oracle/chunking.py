@@ -107,6 +107,24 @@ def split(lengths, bounds):
     return split_chunks, tails, shorts
 
 
+def bucket_order(buckets):
+    """Buckets in the order a short sequence tries them: tot_time /
+    tot_tokens ascending (the share of long sequences in the bucket), ties
+    to the bucket opened first."""
+    return sorted(buckets, key=lambda b: (b["time"] / float(b["tokens"]), b["id"]))
+
+
+def short_order(shorts, alpha1: float, alpha2: float):
+    """Short sequences (sequence, length) by decreasing time, ties to the
+    earlier sequence."""
+    return sorted(shorts, key=lambda js: (-piece_time(0, js[1], alpha1, alpha2), js[0]))
+
+
+def initial_time_threshold(L: int, K: int, alpha1: float, alpha2: float) -> float:
+    """T_t before any loosening: the time of one mesh slice, f(L) / K."""
+    return (alpha1 * float(L * L) + alpha2 * float(L)) / float(K)
+
+
 def chunk(lengths, K: int, alpha1: float, alpha2: float, token_cap: int):
     """Algorithm 1 on one batch of sequence lengths.  Returns a list of
     chunks; each chunk is a dict with 'kind' ('split', 'hybrid' or
@@ -121,7 +139,7 @@ def chunk(lengths, K: int, alpha1: float, alpha2: float, token_cap: int):
     L = max(lengths)
     bounds = mesh(L, min(int(K), L), alpha1, alpha2)
     K = len(bounds) - 1
-    t_t = (alpha1 * float(L * L) + alpha2 * float(L)) / float(K)
+    t_t = initial_time_threshold(L, K, alpha1, alpha2)
     t_m = token_cap
     split_chunks, tails, shorts = split(lengths, bounds)
 
@@ -131,18 +149,14 @@ def chunk(lengths, K: int, alpha1: float, alpha2: float, token_cap: int):
         t = piece_time(c, s, alpha1, alpha2)
         buckets.append({"id": len(buckets), "time": t, "tokens": s, "members": [(j, c, s)], "tail": True})
 
-    def order(bs):
-        return sorted(bs, key=lambda b: (b["time"] / float(b["tokens"]), b["id"]))
-
-    shorts = sorted(shorts, key=lambda js: (-piece_time(0, js[1], alpha1, alpha2), js[0]))
-    for j, n in shorts:
+    for j, n in short_order(shorts, alpha1, alpha2):
         t = piece_time(0, n, alpha1, alpha2)
         while True:
             if not buckets or min(b["tokens"] for b in buckets) + n > t_m:
                 buckets.append({"id": len(buckets), "time": t, "tokens": n, "members": [(j, 0, n)], "tail": False})
                 break
             placed = False
-            for b in order(buckets):
+            for b in bucket_order(buckets):
                 if b["time"] + t <= t_t and b["tokens"] + n <= t_m:
                     b["time"] += t
                     b["tokens"] += n

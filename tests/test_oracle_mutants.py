@@ -88,3 +88,92 @@ def test_gradient_slips_are_caught_by_finite_differences(mut):
     assert np.allclose(target, num, rtol=1e-6, atol=1e-8)
     assert not np.allclose(mine, num, rtol=1e-3, atol=1e-5)
     assert math.isfinite(float(np.sum(mine)))
+
+
+# ----------------------------------------------------------------- chunking
+# Planted slips in the chunking oracle (InfiniPipe section III-B, Algorithm
+# 1); the pages' example, the hand-worked case and the partition equality
+# must catch each.
+
+from oracle import chunking as CH  # noqa: E402
+
+from test_oracle_chunking import _lines  # noqa: E402
+
+
+def _hand_chunks():
+    res = CH.chunk([10, 6, 4, 3, 2], K=2, alpha1=1.0, alpha2=0.0, token_cap=8)
+    return [(c["kind"], c["context"], c["slices"]) for c in res["chunks"]], res["t_t"]
+
+
+def _hand_want():
+    lines = _lines("chunking_hand_example.txt")
+    want = []
+    for ln in lines[2:]:
+        head, slices = ln.split("|")
+        kind, ctx = head.split()
+        want.append((kind, int(ctx), [tuple(int(v) for v in x.split(":")) for x in slices.split()]))
+    return want, float(lines[1].split()[1])
+
+
+def test_chunking_pins_hold_unmutated():
+    assert _hand_chunks() == _hand_want()
+
+
+def test_buckets_tried_by_descending_metric_is_caught(monkeypatch):
+    monkeypatch.setattr(CH, "bucket_order",
+                        lambda bs: sorted(bs, key=lambda b: (-(b["time"] / float(b["tokens"])), b["id"])))
+    assert _hand_chunks() != _hand_want()
+
+
+def test_shorts_by_increasing_time_is_caught(monkeypatch):
+    monkeypatch.setattr(CH, "short_order", lambda shorts, a1, a2: sorted(shorts, key=lambda js: (js[1], js[0])))
+    assert _hand_chunks() != _hand_want()
+
+
+def test_time_threshold_of_the_whole_sequence_is_caught(monkeypatch):
+    monkeypatch.setattr(CH, "initial_time_threshold", lambda L, K, a1, a2: a1 * float(L * L) + a2 * float(L))
+    assert _hand_chunks() != _hand_want()
+
+
+def test_dropped_linear_cost_term_is_caught(monkeypatch):
+    real = CH.mesh
+    monkeypatch.setattr(CH, "mesh", lambda L, K, a1, a2: real(L, K, a1, 0.0))
+    # with alpha1 = alpha2 = 1/2 the mesh must be the FLOPs partition
+    assert any(CH.mesh(L, K, 0.5, 0.5) != PL.partition(L, K) for L in (37, 100, 1000) for K in (2, 3, 5))
+    monkeypatch.setattr(CH, "mesh", real)
+    real_piece = CH.piece_time
+    monkeypatch.setattr(CH, "piece_time", lambda c, s, a1, a2: real_piece(c, s, a1, 0.0))
+    assert CH.piece_time(7, 3, 0.5, 0.5) != float(PL.tri(10) - PL.tri(7))
+
+
+def test_mesh_cut_at_boundaries_not_inside_is_caught(monkeypatch):
+    """Cutting a sequence at boundaries <= L (instead of < L) turns an exact
+    12288-token sequence into 8K + 4K split chunks with an empty tail."""
+    def bad_split(lengths, bounds):
+        inner = bounds[1:-1]
+        sc, tails, shorts = [], [], []
+        for j, L in enumerate(lengths):
+            cuts = [b for b in inner if b <= L]
+            if not cuts:
+                shorts.append((j, L))
+                continue
+            starts = [0] + cuts
+            for a, b in zip(starts[:-1], cuts):
+                sc.append((j, a, b - a))
+            tails.append((j, cuts[-1], L - cuts[-1]))
+        return sc, tails, shorts
+
+    lines = _lines("chunking_mesh_8K4K2K.txt")
+    bounds = [0] + list(np.cumsum([int(x) for x in lines[0].split()[1:]]))
+    pinned = {}
+    for ln in lines[1:]:
+        head, *rest = ln.split("|")
+        L, *parts = head.split()
+        pinned[int(L)] = None if parts == ["short"] else ([int(x) for x in parts], int(rest[0]))
+    monkeypatch.setattr(CH, "split", bad_split)
+    caught = False
+    for L, want in pinned.items():
+        sc, tails, shorts = CH.split([L], bounds)
+        got = None if shorts else ([s for _, _, s in sc], tails[0][2])
+        caught |= got != want
+    assert caught
