@@ -234,7 +234,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
       }
 
       // ---- online softmax (base 2), one query row per lane and subtile.
+      // The row maxima of all subtiles first (their cross-lane steps
+      // overlap), one wave-wide rescale test for all, then the exponentials.
       bf16x8 pf[C::NQ][C::KP];
+      float mxs[C::NQ];
 #pragma unroll
       for (int nq = 0; nq < C::NQ; ++nq) {
         float mx = kNegInf;
@@ -244,19 +247,27 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
           for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[nq][kp][ab][i]);
-        mx = wave_max_xor16_32(mx, xl) * c2;
-        // Lazy rescale: the running maximum m_run only moves when a row's
-        // maximum exceeds it by more than 8 (so every p <= 2^8); softmax is
-        // invariant to the shift, and the final 1/l and LSE use the same m.
-        const bool grow = mx > m_run[nq] + 8.f;
-        if (__any(grow)) {
-          const float m_new = grow ? mx : m_run[nq];
+        mxs[nq] = mx;
+      }
+#pragma unroll
+      for (int nq = 0; nq < C::NQ; ++nq) mxs[nq] = wave_max_xor16_32(mxs[nq], xl) * c2;
+      bool grow_any = false;
+#pragma unroll
+      for (int nq = 0; nq < C::NQ; ++nq) grow_any |= mxs[nq] > m_run[nq] + 8.f;
+      if (__any(grow_any)) {
+#pragma unroll
+        for (int nq = 0; nq < C::NQ; ++nq) {
+          const bool grow = mxs[nq] > m_run[nq] + 8.f;
+          const float m_new = grow ? mxs[nq] : m_run[nq];
           const float alpha = grow ? fast_exp2(m_run[nq] - m_new) : 1.f;  // m_run = -inf -> 0
           l_run[nq] *= alpha;
 #pragma unroll
           for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] *= alpha;
           m_run[nq] = m_new;
         }
+      }
+#pragma unroll
+      for (int nq = 0; nq < C::NQ; ++nq) {
         const float m_use = m_run[nq] == kNegInf ? 0.f : m_run[nq];
         float rs = 0.f;
 #pragma unroll
