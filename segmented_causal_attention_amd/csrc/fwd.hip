@@ -125,12 +125,19 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   const int ke = min(k_hi, r1);
   const int ntiles = ke > kb ? (ke - kb + C::BN - 1) / C::BN : 0;
 
-  float m_run[C::NQ], l_run[C::NQ];
+  float m_run[C::NQ];
+  // Row sums of P on the matrix unit: an extra O^T block whose A operand is
+  // all ones gives sum_k P^T[k][row] in every value of the lane of that row.
+  // It sums the same bf16 P as the numerator, so the normalised weights add
+  // up to one exactly and O's rounding error scales with V's spread around
+  // O rather than with |V|.
+  f32x4 lsum[C::NQ];
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   f32x4 o[C::NQ][C::MT];
 #pragma unroll
   for (int nq = 0; nq < C::NQ; ++nq) {
     m_run[nq] = kNegInf;
-    l_run[nq] = 0.f;
+    lsum[nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
           const bool grow = mxs[nq] > m_run[nq] + 8.f;
           const float m_new = grow ? mxs[nq] : m_run[nq];
           const float alpha = grow ? fast_exp2(m_run[nq] - m_new) : 1.f;  // m_run = -inf -> 0
-          l_run[nq] *= alpha;
+          lsum[nq] *= alpha;
 #pragma unroll
           for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] *= alpha;
           m_run[nq] = m_new;
@@ -269,18 +276,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
 #pragma unroll
       for (int nq = 0; nq < C::NQ; ++nq) {
         const float m_use = m_run[nq] == kNegInf ? 0.f : m_run[nq];
-        float rs = 0.f;
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp)
 #pragma unroll
           for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = fast_exp2(fmaf(s[nq][kp][ab][i], c2, -m_use));
-              s[nq][kp][ab][i] = p;
-              rs += p;
-            }
-        l_run[nq] += rs;
+            for (int i = 0; i < 4; ++i) s[nq][kp][ab][i] = fast_exp2(fmaf(s[nq][kp][ab][i], c2, -m_use));
 #pragma unroll
         for (int kp = 0; kp < C::KP; ++kp) pf[nq][kp] = pack_bf16x8(s[nq][kp][0], s[nq][kp][1]);
       }
@@ -304,6 +305,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
 #pragma unroll
               for (int nq = 0; nq < C::NQ; ++nq) o[nq][mt] = mfma16(vf.f[kp], pf[nq][kp], o[nq][mt]);
           });
+#pragma unroll
+      for (int kp = 0; kp < C::KP; ++kp)
+#pragma unroll
+        for (int nq = 0; nq < C::NQ; ++nq) lsum[nq] = mfma16(ones, pf[nq][kp], lsum[nq]);
     }
     ++j;
     return j < ntiles;
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   OutT *__restrict__ og = static_cast<OutT *>(a.o);
 #pragma unroll
   for (int nq = 0; nq < C::NQ; ++nq) {
-    const float lt = wave_sum_xor16_32(l_run[nq], xl);
+    const float lt = lsum[nq][0];
     const int qrow = rw0 + 16 * nq + l16;
     const bool valid = has_rows && qrow < r1;
     const float lse_new = lt > 0.f ? (m_run[nq] + fast_log2(lt)) * kLn2 : kNegInf;
