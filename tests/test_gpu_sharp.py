@@ -23,12 +23,14 @@ DEV = "cuda"
 
 # dQ_i = scale sum_j dS_ij K_j, and sum_j dS_ij = 0 exactly over a row's
 # visible keys, so dQ only depends on how K varies across the few keys a row
-# attends to.  The kernels round dS to bf16 (unit roundoff 2^-9) for the
-# matrix product; when the keys share a component much larger than that
-# variation (here the rising ramp, up to 1.5 T along one axis), the rounding
-# errors no longer cancel and dQ's relative error grows like
-# 2^-9 |K| / (K's variation over the ~1 / (step scale ln 2) keys a row sees):
-# measured 0.09-0.19 for these inputs.  dK and dV have no such cancellation.
+# attends to.  Two roundings of relative size 2^-9 break that sum: dS is
+# rounded to bf16 for the matrix product, and D = <dO, O> comes from the
+# forward's O, whose P was rounded to bf16 while the backward recomputes P in
+# fp32.  When the keys share a component much larger than their variation
+# (here the rising ramp, up to 1.5 T along one axis), dQ's relative error
+# grows like 2^-9 |K| / (K's variation over the ~1 / (step scale ln 2) keys a
+# row sees): measured 0.09-0.19 for these inputs.  dK and dV have no such
+# cancellation.
 RAMP_DQ_REL_L2 = 0.3
 
 
