@@ -1,10 +1,10 @@
 """Benchmark of the segmented causal attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c4tail|c5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload seg32k|ring128k|varlen256k|varlen256k_tail|seg1m] [--no-cpu-baseline]
                     [--no-hbm-kernels]
     python bench.py --sweep-segments
     python bench.py --offload
-    python bench.py --latency-c1
+    python bench.py --latency-small
     python bench.py --chunking
 
 --sweep-segments times the same fwd+bwd path on 131072 tokens (32 heads,
@@ -18,7 +18,7 @@ N instead of the single benchmark line.
 GPU, and times it chunk by chunk (one JSON line for the fit, then one per
 plan).
 
---latency-c1 times the small oracle-identity case (1024 tokens, one head,
+--latency-small times the small oracle-identity case (1024 tokens, one head,
 d = 64, fp32 inputs, 4 FLOPs-balanced segments, forward only), which is
 launch-bound: GPU time and host wall time per call, one JSON line.
 
@@ -100,13 +100,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c4tail", "c5"])
+    p.add_argument("--workload", default="seg32k", choices=["seg32k", "ring128k", "varlen256k", "varlen256k_tail", "seg1m"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-hbm-kernels", action="store_true",
                    help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
                    help="token prefix of one head timed for the CPU oracle baseline")
-    p.add_argument("--latency-c1", action="store_true",
+    p.add_argument("--latency-small", action="store_true",
                    help="per-call latency of the 1024-token, 1-head, d=64 fp32 forward (one line)")
     p.add_argument("--offload", action="store_true",
                    help="per-segment fwd/bwd with Q/O/LSE offloaded to host memory and prefetched (one line)")
@@ -125,18 +125,18 @@ class Workload:
     """Inputs, items and preallocated outputs of one benchmark workload."""
 
     def __init__(self, name, torch, sa, synth):
-        if name == "c4tail":
+        if name == "varlen256k_tail":
             # the varlen batch at its tail seed: the least seed >= 1004 whose
             # draw holds a sequence of 64K-128K tokens
             seed = synth.tail_seed()
-            w = dict(synth.WORKLOADS["c4"], seed=seed)
+            w = dict(synth.WORKLOADS["varlen256k"], seed=seed)
             w["name"] = f"{w['name']}_seed{seed}"
-            name = "c4"
+            name = "varlen256k"
         else:
             w = synth.WORKLOADS[name]
         self.name, self.w = name, w
         self.hq, self.hkv, self.d = w["hq"], w["hkv"], w["d"]
-        if name == "c4":
+        if name == "varlen256k":
             lens = synth.lognormal_lengths(w["seed"], total=w["T"])
             self.cu = synth.cu_seqlens(lens)
             self.T = int(self.cu[-1])
@@ -147,7 +147,7 @@ class Workload:
             self.cu = None
         t = synth.gen_tensors(w["seed"], self.T, self.hq, self.hkv, self.d, dtype="bf16", device="cuda")
         self.q, self.k, self.v, self.do = t["q"], t["k"], t["v"], t["do"]
-        self.ring = name == "c3"
+        self.ring = name == "ring128k"
         o_dtype = torch.float32 if self.ring else torch.bfloat16
         self.o = torch.empty((self.T, self.hq, self.d), dtype=o_dtype, device="cuda")
         self.lse = torch.empty((self.hq, self.T), dtype=torch.float32, device="cuda")
@@ -167,7 +167,7 @@ class Workload:
 
     def plan(self):
         sa, w = self.sa_mod(), self.w
-        if self.name == "c4":
+        if self.name == "varlen256k":
             return sa.segattn_partition_varlen(self.cu, w["max_slice"])
         b = sa.segattn_partition(w["S"], w["N"])
         if self.ring:
@@ -369,7 +369,7 @@ def chunking_bench(torch, sa, synth, reps=3, token_cap=16384, ks=(1, 2, 3, 4, 5)
     per-chunk fwd+bwd time max / mean (the balance the algorithm aims at),
     total time and TFLOP/s.  The slicing rule of the main benchmark (16384-
     token FLOPs-balanced slices) runs the same way with each item as a chunk."""
-    W = Workload("c4", torch, sa, synth)
+    W = Workload("varlen256k", torch, sa, synth)
     q, k, v, do, hq, d, T = W.q, W.k, W.v, W.do, W.hq, W.d, W.T
     shape = sa.make_shape(q, k)
     o = torch.empty((T, hq, d), dtype=torch.bfloat16, device="cuda")
@@ -436,7 +436,7 @@ def c1_latency(torch, sa, synth, calls=500, warmup=50):
     items).  GPU time: HIP events around `calls` back-to-back calls on the
     launch stream.  Host time: wall clock of the same calls, including the
     host-side checks, table upload and launch, until the stream drains."""
-    w = synth.WORKLOADS["c1"]
+    w = synth.WORKLOADS["seg1k_fp32"]
     S, N, d = w["S"], w["N"], w["d"]
     t = synth.gen_tensors(w["seed"], S, w["hq"], w["hkv"], d, dtype="fp32", device="cuda")
     q, k, v = t["q"], t["k"], t["v"]
@@ -470,7 +470,7 @@ def offload_bench(torch, sa, synth, reps=5):
     per-segment schedule, and the per-segment schedule with offloading; plus
     the device -> host bandwidth that sets the per-stage transfer volume
     (threshold = bandwidth x one balanced segment's forward time)."""
-    W = Workload("c2", torch, sa, synth)
+    W = Workload("seg32k", torch, sa, synth)
     T, hq, d = W.T, W.hq, W.d
     b = [int(x) for x in sa.segattn_partition(T, W.w["N"])]
     N = len(b) - 1
@@ -614,7 +614,7 @@ def main():
     if args.offload:
         offload_bench(torch, sa, synth)
         return
-    if args.latency_c1:
+    if args.latency_small:
         c1_latency(torch, sa, synth)
         return
     if args.chunking:

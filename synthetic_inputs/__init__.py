@@ -29,15 +29,15 @@ import torch
 
 # Workloads: one causal attention layer, batch 1, synthetic N(0,1) inputs.
 WORKLOADS = {
-    "c1": dict(name="S1024_H1_d64_N4_fp32_fwd", S=1024, hq=1, hkv=1, d=64, N=4,
+    "seg1k_fp32": dict(name="S1024_H1_d64_N4_fp32_fwd", S=1024, hq=1, hkv=1, d=64, N=4,
                dtype="fp32", seed=1001, fwd_only=True),
-    "c2": dict(name="S32768_H32_d128_N8_bf16", S=32768, hq=32, hkv=32, d=128, N=8,
+    "seg32k": dict(name="S32768_H32_d128_N8_bf16", S=32768, hq=32, hkv=32, d=128, N=8,
                dtype="bf16", seed=1002, fwd_only=False),
-    "c3": dict(name="S131072_H32_d128_N16_ring16384_bf16", S=131072, hq=32, hkv=32,
+    "ring128k": dict(name="S131072_H32_d128_N16_ring16384_bf16", S=131072, hq=32, hkv=32,
                d=128, N=16, block=16384, dtype="bf16", seed=1003, fwd_only=False),
-    "c4": dict(name="varlen262144_Hq32_Hkv8_d128_slice16384_bf16", T=262144, hq=32,
+    "varlen256k": dict(name="varlen262144_Hq32_Hkv8_d128_slice16384_bf16", T=262144, hq=32,
                hkv=8, d=128, max_slice=16384, dtype="bf16", seed=1004, fwd_only=False),
-    "c5": dict(name="S1048576_H40_d128_N64_bf16", S=1048576, hq=40, hkv=40, d=128,
+    "seg1m": dict(name="S1048576_H40_d128_N64_bf16", S=1048576, hq=40, hkv=40, d=128,
                N=64, dtype="bf16", seed=1005, fwd_only=False),
 }
 

@@ -110,7 +110,7 @@ def _bwd(q, k, v, o, lse, do, items):
 # ------------------------------------------------------------ ring workload
 
 def test_ring_131072_full_size():
-    w = WORKLOADS["c3"]
+    w = WORKLOADS["ring128k"]
     S, H, d, N, B = w["S"], w["hq"], w["d"], w["N"], w["block"]
     scale = 1 / math.sqrt(d)
     say(f"case ring full seed={w['seed']} S={S} H={H} d={d} N={N} block={B}")
@@ -140,7 +140,7 @@ def test_ring_131072_full_size():
 
 @pytest.mark.parametrize("which", ["typical", "tail"])
 def test_varlen_262144_full_size(which):
-    w = WORKLOADS["c4"]
+    w = WORKLOADS["varlen256k"]
     seed = w["seed"] if which == "typical" else tail_seed(w["seed"])
     hq, hkv, d, cap = w["hq"], w["hkv"], w["d"], w["max_slice"]
     scale = 1 / math.sqrt(d)
@@ -186,7 +186,7 @@ def test_varlen_262144_full_size(which):
 
 @pytest.fixture(scope="module")
 def million():
-    w = WORKLOADS["c5"]
+    w = WORKLOADS["seg1m"]
     say(f"case million inputs seed={w['seed']} S={w['S']} H={w['hq']} d={w['d']}")
     t = gen_tensors(w["seed"], w["S"], w["hq"], w["hkv"], w["d"], device=DEV)
     torch.cuda.synchronize()

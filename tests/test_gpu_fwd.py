@@ -28,8 +28,8 @@ def _bf16_host(t):
 
 
 def test_c1_segmented_fp32_inputs():
-    w = WORKLOADS["c1"]
-    say(f"case c1 seed={w['seed']} S={w['S']} d={w['d']} N={w['N']} fp32")
+    w = WORKLOADS["seg1k_fp32"]
+    say(f"case seg1k_fp32 seed={w['seed']} S={w['S']} d={w['d']} N={w['N']} fp32")
     q, k, v = _inputs(w["seed"], w["S"], 1, 1, w["d"], dtype="fp32")
     b = sa.segattn_partition(w["S"], w["N"])
     assert b.tolist() == [0, 512, 724, 887, 1024]
@@ -176,9 +176,9 @@ def test_indexing_probe_zero_keys():
 
 
 def test_c2_full_size_sampled_rows():
-    w = WORKLOADS["c2"]
+    w = WORKLOADS["seg32k"]
     S, H, d = w["S"], w["hq"], w["d"]
-    say(f"case c2 full seed={w['seed']} S={S} H={H} d={d} N={w['N']}")
+    say(f"case seg32k full seed={w['seed']} S={S} H={H} d={d} N={w['N']}")
     q, k, v = _inputs(w["seed"], S, H, H, d)
     b = sa.segattn_partition(S, w["N"])
     o, lse = sa.segattn_fwd(q, k, v, segments(b), o_dtype=torch.bfloat16)
