@@ -29,7 +29,7 @@ def _draw(seed):
     while True:
         d = int(rng.choice([64, 128]))
         hkv = int(rng.choice([1, 2, 3]))
-        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        hq = hkv * int(rng.choice([1, 2, 3, 4, 6, 8]))
         kind = str(rng.choice(["segments", "varlen", "ring"]))
         cfg = dict(seed=seed, d=d, hq=hq, hkv=hkv, kind=kind,
                    in_dtype="fp32" if rng.random() < 0.2 else "bf16",
@@ -61,7 +61,7 @@ def _draw(seed):
         return cfg
 
 
-@pytest.mark.parametrize("seed", range(5000, 5024))
+@pytest.mark.parametrize("seed", range(5000, 5048))
 def test_random_path(seed):
     c = _draw(seed)
     T, hq, hkv, d, scale = c["T"], c["hq"], c["hkv"], c["d"], c["scale"]
