@@ -182,6 +182,47 @@ def test_varlen_262144_full_size(which):
     _check_invariants(do, dk, dv, cu, hq, hkv, "varlen")
 
 
+def test_varlen_262144_chunked_schedule_full_size():
+    """The same 262144-token batch (tail seed: longest sequence 77309) in the
+    workload-balanced chunks of InfiniPipe section III-B, Algorithm 1 (K = 4,
+    token cap 16384): one forward launch per chunk, then one backward launch
+    per chunk in reverse with fp32 gradients accumulating across launches.
+    Sampled rows at every chunk boundary of the longest sequence, tail keys
+    and the invariants, against the float64 oracle."""
+    w = WORKLOADS["varlen256k"]
+    seed = tail_seed(w["seed"])
+    hq, hkv, d = w["hq"], w["hkv"], w["d"]
+    scale = 1 / math.sqrt(d)
+    lens = lognormal_lengths(seed, total=w["T"])
+    cu = cu_seqlens(lens)
+    T = int(cu[-1])
+    items, owner, nch, _ = sa.segattn_chunk_varlen(cu, 4, 1.0, 256.0, 16384)
+    say(f"case varlen chunked full seed={seed} T={T} max_len={max(lens)} chunks={nch} items={len(items)}")
+    t = gen_tensors(seed, T, hq, hkv, d, device=DEV)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    chunks = [items[owner == c] for c in range(nch)]
+    o = torch.empty((T, hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((hq, T), dtype=torch.float32, device=DEV)
+    for ch in chunks:
+        sa.segattn_fwd(q, k, v, ch, o=o, lse=lse)
+    dq, dk, dv = (torch.zeros(x.shape, dtype=torch.float32, device=DEV) for x in (q, k, v))
+    for ch in reversed(chunks):
+        sa.segattn_bwd(q, k, v, o, lse, do, ch[::-1].copy(), dq=dq, dk=dk, dv=dv, accumulate=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed + 7)
+    s = int(np.argmax(lens))
+    a, L = int(cu[s]), int(lens[s])
+    cuts = sorted({int(it[1]) for it in items.tolist() if it[0] == a} | {int(it[2]) for it in items.tolist() if it[0] == a})
+    assert len(cuts) >= 4, cuts  # the longest sequence is split by the mesh
+    rows = np.unique(np.clip(np.concatenate([[0, L - 1], cuts, np.asarray(cuts) - 1, rng.integers(0, L, 10)]),
+                             0, L - 1))
+    what = f"chunked seq{s}(L={L})"
+    for h in (0, hq - 1):
+        _check_rows(q, k, v, do, o, lse, dq, a, L, h, oracle.kv_head_of(h, hq, hkv), rows, scale, what)
+    _check_tail_keys(q, k, v, do, dk, dv, a, L, hkv - 1, hq, hkv, 32, scale, what)
+    _check_invariants(do, dk, dv, cu, hq, hkv, "chunked varlen")
+
+
 # ---------------------------------------------------------- 1M-token share
 
 @pytest.fixture(scope="module")
