@@ -101,3 +101,26 @@ def test_offload_round_trip_keeps_gradients(T, hq, hkv, N, frac):
         g = got.float().cpu().numpy().astype(np.float64)
         rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
         assert rel <= 1e-2, f"{name} rel-L2 {rel:.3g}"
+
+
+def test_offload_round_trip_full_size():
+    """The 32768-token, 32-head, 8-segment workload (the bench's offload
+    case): with the planned share of every segment's Q, O and LSE rows moved
+    to pinned host memory and back (33-100 MiB per segment), O, LSE and all
+    gradients stay bit-identical to the schedule without offloading."""
+    T, hq, hkv, d, N = 32768, 32, 32, 128, 8
+    say(f"case offload full size T={T} hq={hq} N={N}")
+    t = gen_tensors(32, T, hq, hkv, d, dtype="bf16", device=DEV)
+    bounds = [int(x) for x in sa.segattn_partition(T, N)]
+    L = [bounds[i + 1] - bounds[i] for i in range(N)]
+    row_bytes = hq * d * 2 * 2 + hq * 4
+    alpha, moved, mem, peak = sa.segattn_offload_plan(L, row_bytes, 0.55 * max(L) * row_bytes)
+    moved = [int(x) for x in moved]
+    moved[-1] = 0
+    say(f"  rows moved per segment {moved}")
+    assert sum(moved) > 0
+    base = _run(t["q"].clone(), t["k"], t["v"], t["do"], bounds)
+    off = _run(t["q"].clone(), t["k"], t["v"], t["do"], bounds, offload_rows=moved)
+    assert off[5], "offloaded device rows were not cleared before the prefetch"
+    for a, b, name in zip(base[:5], off[:5], ("O", "LSE", "dQ", "dK", "dV")):
+        assert torch.equal(a, b), f"{name} differs after the offload round trip"
