@@ -72,7 +72,7 @@ struct PreArgs {
 // reverse).  kv units: one per (kv group, 128-key tile); kv group g covers
 // keys [kb, ke) of one sequence, stored as rows of kvg (4 int32):
 //   [0] seq_off [1] kb [2] ke [3] unit_begin
-// q units: one per (q group, 128-row tile); q group = a run of adjacent items
+// q units: one per (q group, 256-row tile); q group = a run of adjacent items
 // with identical query ranges, stored as rows of qg (4 int32):
 //   [0] first item  [1] item count  [2] unit_begin  [3] unused
 struct BwdArgs {
