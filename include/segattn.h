@@ -227,6 +227,14 @@ int segattn_bwd_preprocess(const segattn_shape *shape, const void *o, int32_t o_
  * item's key range are overwritten (other rows untouched); with it g_dtype
  * must be F32 and the gradients are added.  workspace: device, >=
  * segattn_bwd_workspace bytes.
+ * dQ is evaluated as dQ_q = scale sum_j dS_qj (K_j - K_q), keys measured
+ * from the query row's own key K_q.  That is the same value (sum_j dS_qj = 0
+ * over a row's visible keys), and it keeps a component that all keys share
+ * out of dQ's rounding error.  So a call's dQ is the full gradient only for
+ * rows whose visible keys the call's items cover completely (as one call
+ * over all items, or the per-segment calls of a reverse-order schedule,
+ * do); calls that split one row's keys between them sum to it exactly, but
+ * each one alone is not the gradient through its own keys.
  * Errors: E_INVALID, E_UNSUPPORTED, E_RANGE, E_WORKSPACE, E_DEVICE. */
 int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const void *v,
                 const void *o, int32_t o_dtype, const float *lse, const void *d_o,

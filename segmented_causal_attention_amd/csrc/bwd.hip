@@ -33,6 +33,16 @@
 //   registers) and walks the 64-key tiles of every item of its query group;
 //   per tile it recomputes S^T, P, dP^T - D, dS^T and accumulates dQ^T
 //   (3 products).
+//   Keys are measured from the query row's own key: dQ_i = scale sum_j dS_ij
+//   (K_j - K_i).  The two forms agree exactly because a row's dS sums to zero
+//   over its visible keys (softmax is shift invariant).  In floating point
+//   they do not: dS is rounded to bf16 for the product, and D comes from the
+//   forward's O (built from bf16 P) while P here is fp32, so the computed dS
+//   of a row misses zero by about 2^-9 of its size.  Multiplied by K_j, that
+//   miss carries every component the keys share; multiplied by K_j - K_i, only
+//   how the keys vary near the row.  The row sum R_i of the bf16 dS values
+//   that enter the product is accumulated beside it (v_dot2 against ones),
+//   and the epilogue subtracts R_i K_i from sum_j dS_ij K_j.
 #include <type_traits>
 
 #include "device_common.h"
@@ -587,6 +597,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   const int rw0 = r0 + 32 * wave;
   const int rw_end = min(rw0 + 32, r1);
   const bool has_rows = rw0 < rw_end;
+  const int mkey = -8 * lg, mrow = l16 + mkey;  // lane constants of the mask
 
   bf16x8 qf[2][C::KS], dof[2][C::KS];
   float lse2[2], ndrow[2];  // LSE (base 2) and -D of the lane's two rows
@@ -607,21 +618,21 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   }
 
   f32x4 dq[2][C::NT];
+  // Per-lane share of R = sum over keys of the bf16 dS of a row: lane
+  // (l16, lg) holds keys 8lg .. 8lg+7 of each 32-key pair of rows 16nq + l16.
+  float rsum[2] = {0.f, 0.f};
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) dq[nq][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
 
-  // Loop-invariant LDS byte offsets of this lane's reads.
-  int rkoff[C::KS], rvoff[C::KS], coff[C::NT];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    rkoff[ks] = row_read_off<D, kColTile>(ks, l16, lg);
-    rvoff[ks] = row_read_off<D, kRowTile>(ks, l16, lg);
-  }
-#pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) coff[nt] = col_read_off<D>(nt, l16, lg);
+  // Loop-invariant LDS byte offsets of this lane's reads: step 0 only, the
+  // other steps by XOR (row_step / col_step), which keeps this role's
+  // register count within two wavefronts per SIMD.
+  const int rkoff = row_read_off<D, kColTile>(0, l16, lg);
+  const int rvoff = row_read_off<D, kRowTile>(0, l16, lg);
+  const int coff = col_read_off<D>(0, l16, lg);
 
   const int64_t kstride = (int64_t)hkv * D;
   // The fragment loads above complete here, before the first tile copy: the
@@ -687,28 +698,33 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
             // dP^T starts from -D of the lane's query row: it yields dP - D
             dp[nq][ab] = (f32x4){ndrow[nq], ndrow[nq], ndrow[nq], ndrow[nq]};
           }
-        // sub-step ks: the K and V row fragments of depth step ks
-        pipelined<C::KS>(
-            [&](auto ksc) __attribute__((always_inline)) {
-              constexpr int ks = decltype(ksc)::value;
+        // sub-steps 0 .. KS-1: the K row fragments of depth step ks (S^T);
+        // KS .. 2KS-1: the V row fragments (dP^T).  One operand kind per
+        // sub-step keeps half as many fragments in flight as loading both.
+        pipelined<2 * C::KS>(
+            [&](auto ic) __attribute__((always_inline)) {
+              constexpr int ks = decltype(ic)::value % C::KS;
+              constexpr bool is_v = decltype(ic)::value >= C::KS;
               struct {
-                bf16x8 k[2], v[2];
+                bf16x8 f[2];
               } f;
 #pragma unroll
-              for (int ab = 0; ab < 2; ++ab) {
-                f.k[ab] = lds_row8(Ks, rkoff[ks] + (32 * kp + 4 * ab) * 2 * D);
-                f.v[ab] = lds_row8(Vs, rvoff[ks] + (32 * kp + 4 * ab) * 2 * D);
-              }
+              for (int ab = 0; ab < 2; ++ab)
+                f.f[ab] = is_v ? lds_row8(Vs, (rvoff ^ row_step(ks)) + (32 * kp + 4 * ab) * 2 * D)
+                               : lds_row8(Ks, (rkoff ^ row_step(ks)) + (32 * kp + 4 * ab) * 2 * D);
               return f;
             },
-            [&](auto ksc, const auto &f) __attribute__((always_inline)) {
-              constexpr int ks = decltype(ksc)::value;
+            [&](auto ic, const auto &f) __attribute__((always_inline)) {
+              constexpr int ks = decltype(ic)::value % C::KS;
+              constexpr bool is_v = decltype(ic)::value >= C::KS;
 #pragma unroll
               for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
                 for (int nq = 0; nq < 2; ++nq) {
-                  s[nq][ab] = mfma16(f.k[ab], qf[nq][ks], s[nq][ab]);
-                  dp[nq][ab] = mfma16(f.v[ab], dof[nq][ks], dp[nq][ab]);
+                  if constexpr (is_v)
+                    dp[nq][ab] = mfma16(f.f[ab], dof[nq][ks], dp[nq][ab]);
+                  else
+                    s[nq][ab] = mfma16(f.f[ab], qf[nq][ks], s[nq][ab]);
                 }
             });
         if (kp == 0) stage_if();
@@ -717,7 +733,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
         auto make_ds = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq) {
-            const int qrow = rw0 + 16 * nq + l16;
             f32x4 ds[2];
 #pragma unroll
             for (int ab = 0; ab < 2; ++ab)
@@ -725,10 +740,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
               for (int i = 0; i < 4; ++i) {
                 float arg = fmaf(s[nq][ab][i], c2, -lse2[nq]);
                 if constexpr (decltype(maskc)::value) {
-                  // key kv0 + 32kp + 8lg + c (c = 4ab + i) is visible iff
-                  // c <= min(qrow, k_hi - 1) - kv0 - 32kp - 8lg: the sign of
-                  // the difference picks a +inf / -inf bound (no compares)
-                  const int lim = min(qrow, k_hi - 1) - kv0 - 32 * kp - 8 * lg;
+                  // key kv0 + 32kp + 8lg + c (c = 4ab + i) is visible to row
+                  // qrow = rw0 + 16nq + l16 iff c <= min(qrow, k_hi - 1) - kv0
+                  // - 32kp - 8lg, written with the two per-lane constants
+                  // mrow = l16 - 8lg and mkey = -8lg: the sign of the
+                  // difference picks a +inf / -inf bound (no compares)
+                  const int lim = min(rw0 + 16 * nq + mrow, k_hi - 1 + mkey) - kv0 - 32 * kp;
                   const uint32_t sign = (uint32_t)(lim - (4 * ab + i)) & 0x80000000u;
                   arg = fminf(arg, __builtin_bit_cast(float, sign | 0x7f800000u));
                 }
@@ -752,7 +769,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
               bf16x8 f[2];
             } ka;
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) ka.f[kp] = lds_col8<D>(Ks, coff[nt] + 32 * kp * 2 * D);
+            for (int kp = 0; kp < 2; ++kp) ka.f[kp] = lds_col8<D>(Ks, (coff ^ col_step(nt)) + 32 * kp * 2 * D);
             return ka;
           },
           [&](auto ntc, const auto &ka) __attribute__((always_inline)) {
@@ -762,6 +779,22 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
 #pragma unroll
               for (int nq = 0; nq < 2; ++nq) dq[nq][nt] = mfma16(ka.f[kp], dsb[nq][kp], dq[nq][nt]);
           });
+      // ---- this tile's share of R (the bf16 dS values of the product
+      // above), after the product is issued so that it runs beside it; two
+      // independent chains per row halve the dependent latency.  (Adding it
+      // into per-lane LDS slots with ds_add_f32 instead, to save the two
+      // registers, made the backward 14% slower.)
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        float t[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const u32x4 w = __builtin_bit_cast(u32x4, dsb[nq][kp]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[kp] = sum_bf16x2(w[e], t[kp]);
+        }
+        rsum[nq] += t[0] + t[1];
+      }
     }
     stage_if();
     cp = walk.advance(cp);
@@ -772,15 +805,24 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
     while (ring_pass<0, NS>(step)) {
     }
 
-  // ---- epilogue: lane holds dQ[row = rw0 + 16nq + l16][16nt + 4lg + i]
+  // ---- epilogue: lane holds dQ[row = rw0 + 16nq + l16][16nt + 4lg + i];
+  // subtract R_row K_row (the bf16 values the products used), then scale.
   GT *dqg = static_cast<GT *>(a.dq);
+  const XorLanes xl(lane);
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq) {
     const int row = rw0 + 16 * nq + l16;
+    // the row's four lane shares (lanes l16 + 16 lg), in a fixed order
+    const float r = wave_sum_xor16_32(rsum[nq], xl);
     if (has_rows && row < r1) {
-      GT *p = dqg + (((int64_t)seq_off + row) * hq + h) * D + 4 * lg;
+      const int64_t grow = (int64_t)seq_off + row;
+      const InT *kp = kg + (grow * hkv + g) * D + 4 * lg;
+      GT *p = dqg + (grow * hq + h) * D + 4 * lg;
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) put4<GT>(p + 16 * nt, dq[nq][nt] * a.scale, a.accumulate);
+      for (int nt = 0; nt < C::NT; ++nt) {
+        const f32x4 kr = load4_bf16<InT>(kp + 16 * nt);
+        put4<GT>(p + 16 * nt, (dq[nq][nt] - r * kr) * a.scale, a.accumulate);
+      }
     }
   }
 }

@@ -74,6 +74,29 @@ __device__ __forceinline__ bf16x8 lds_rows8(const __bf16 *tile, int stride, int 
   return __builtin_bit_cast(bf16x8, (s16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
+// c + lo + hi of the two bf16 values packed in w (v_dot2 against ones; the
+// products are exact, the sum is fp32).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), c,
+                                         false);
+}
+
+// 4 consecutive input elements as floats holding their bf16 values (fp32
+// input is rounded to nearest-even bf16, as when it is staged).
+template <typename InT>
+__device__ __forceinline__ f32x4 load4_bf16(const InT *p);
+template <>
+__device__ __forceinline__ f32x4 load4_bf16<__bf16>(const __bf16 *p) {
+  const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+  return (f32x4){bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
+template <>
+__device__ __forceinline__ f32x4 load4_bf16<float>(const float *p) {
+  const f32x4 x = *reinterpret_cast<const f32x4 *>(p);
+  const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
+  return (f32x4){bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+}
+
 // Byte-select of two dwords: result byte i = byte sel_i of {hi:lo}.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

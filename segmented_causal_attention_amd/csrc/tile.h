@@ -122,6 +122,16 @@ __device__ __forceinline__ int col_read_off(int mt, int l16, int lg) {
   return chunk_off<D, kColTile>(r, c) + 8 * (l16 & 1);
 }
 
+// The offsets of the other depth steps / column blocks follow from step 0 by
+// an XOR: the step index only flips offset bits that the swizzle XORs and no
+// other term sets (bits 6-7 for row reads, 5-7 for transposing reads, both
+// at D = 64 and 128):
+//   row_read_off(ks) == row_read_off(0) ^ row_step(ks),
+//   col_read_off(mt) == col_read_off(0) ^ col_step(mt).
+// A kernel short of registers keeps only the step-0 offsets.
+__device__ __forceinline__ constexpr int row_step(int ks) { return ks << 6; }
+__device__ __forceinline__ constexpr int col_step(int mt) { return mt << 5; }
+
 __device__ __forceinline__ const char *lds_at(const void *base, int byte_off) {
   return static_cast<const char *>(base) + byte_off;
 }
@@ -164,31 +174,39 @@ struct TileLoader<D, __bf16, W> {
   static constexpr int NI = kTileRows / RPI / W;  // instructions per wavefront
   static constexpr int kInstr = NI;
   static_assert(NI >= 1 && NI * RPI * W == kTileRows, "tile split");
-  int row_[NI];          // lane's tile row per instruction
-  uint32_t boff_[2][NI];  // byte offset of the lane's chunk in a full tile, per tile kind
-  uint32_t rbytes_;       // bytes between rows (64 rows < 2^32 bytes: heads <= 65536, d <= 128)
-  int wave_;              // wavefront index (scalar)
+  // Instruction t copies the rows of instruction 0 plus t * RPI.  With NI <= 2
+  // and RPI = 4 that only sets row bit 2, which neither swizzle reads, so its
+  // lane offsets are instruction 0's plus t * RPI rows: that part goes on the
+  // scalar base and the lanes keep one offset per tile kind.
+  static_assert(NI == 1 || (NI == 2 && RPI == 4), "later instructions must keep the lane's swizzled chunk");
+  int row0_;          // lane's tile row in instruction 0
+  uint32_t boff_[2];  // byte offset of the lane's chunk in a full tile, per tile kind
+  uint32_t rbytes_;   // bytes between rows (64 rows < 2^32 bytes: heads <= 65536, d <= 128)
+  int wave_;          // wavefront index (scalar)
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
     rbytes_ = 2u * (uint32_t)stride;
     wave_ = wave;
-#pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      row_[t] = (wave * NI + t) * RPI + lane / CPR;
-      boff_[kRowTile][t] = row_[t] * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kRowTile>(row_[t]));
-      boff_[kColTile][t] = row_[t] * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kColTile>(row_[t]));
-    }
+    row0_ = wave * NI * RPI + lane / CPR;
+    boff_[kRowTile] = row0_ * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kRowTile>(row0_));
+    boff_[kColTile] = row0_ * rbytes_ + 16u * ((lane % CPR) ^ swz<D, kColTile>(row0_));
   }
   template <int KIND>
   __device__ __forceinline__ void stage(__bf16 *, uint32_t tile, const __bf16 *src, int nvalid) const {
     if (nvalid >= kTileRows) {
       // full tile: the precomputed lane offsets as they are
 #pragma unroll
-      for (int t = 0; t < NI; ++t) dma_to_lds<16>(src, boff_[KIND][t], tile + (wave_ * NI + t) * RPI * D * 2);
+      for (int t = 0; t < NI; ++t)
+        dma_to_lds<16>(reinterpret_cast<const char *>(src) + (size_t)(t * RPI) * rbytes_, boff_[KIND],
+                       tile + (wave_ * NI + t) * RPI * D * 2);
     } else {
-      // partial tile: rows >= nvalid repeat the last valid row
+      // partial tile: rows >= nvalid repeat the last valid row.  The lane
+      // offset is an unsigned 32-bit byte offset from the unshifted base, so
+      // it is formed as min(row, nvalid - 1) rows plus the lane's chunk,
+      // never as a difference that could go below zero.
+      const uint32_t chunk = boff_[KIND] - (uint32_t)row0_ * rbytes_;
 #pragma unroll
       for (int t = 0; t < NI; ++t)
-        dma_to_lds<16, true>(src, boff_[KIND][t] - (uint32_t)max(0, row_[t] - (nvalid - 1)) * rbytes_,
+        dma_to_lds<16, true>(src, (uint32_t)min(row0_ + t * RPI, nvalid - 1) * rbytes_ + chunk,
                              tile + (wave_ * NI + t) * RPI * D * 2);
     }
   }
