@@ -61,6 +61,30 @@ def make_shape(q, k, scale=None):
     return Shape(q.shape[0], q.shape[1], k.shape[1], d, _DTYPE_CODE[q.dtype], sc)
 
 
+def _same(t, name, shape, dtype=None, dtypes=None):
+    """Raises unless t has exactly `shape` (and `dtype`, or one of `dtypes`).
+    The C layer only sees pointers, so every buffer's size and element type
+    is checked here, before anything is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+
+
+def _check_kv(q, k, v):
+    _same(v, "v", k.shape, k.dtype)
+
+
+def _check_stats(q, o, lse):
+    """o [T, hq, d] in bf16 or fp32; lse [hq, T] fp32."""
+    _same(o, "o", q.shape, dtypes=(torch.bfloat16, torch.float32))
+    _same(lse, "lse", (q.shape[1], q.shape[0]), torch.float32)
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is None:
         return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
@@ -140,12 +164,14 @@ def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, m
     New outputs are allocated (o_dtype defaults to q's dtype; lse filled
     with -inf) when not given."""
     shape = make_shape(q, k, scale)
+    _check_kv(q, k, v)
     arr, p, n = _items_arg(items)
     if o is None:
         od = _CODE_DTYPE[o_dtype] if isinstance(o_dtype, int) else (o_dtype or q.dtype)
         o = torch.zeros((q.shape[0], q.shape[1], q.shape[2]), dtype=od, device=q.device)
     if lse is None:
         lse = torch.full((q.shape[1], q.shape[0]), -math.inf, dtype=torch.float32, device=q.device)
+    _check_stats(q, o, lse)
     ocode = _DTYPE_CODE[o.dtype]
     ws = _workspace(segattn_fwd_workspace(shape, arr), q.device, workspace)
     flags = SEGATTN_MERGE_INTO if merge_into else 0
@@ -162,12 +188,30 @@ def segattn_merge(o_a, lse_a, o_b, lse_b, *, o_out=None, lse_out=None, rows=None
         o_out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    if not isinstance(o_a, torch.Tensor) or o_a.dim() != 3:
+        raise ValueError("o_a must be [rows, h, d]")
+    if not isinstance(lse_a, torch.Tensor) or lse_a.dim() != 2:
+        raise ValueError("lse_a must be [h, stride]")
+    for t, nm in ((o_b, "o_b"), (o_out, "o_out")):
+        _same(t, nm, o_a.shape, torch.float32)
+    _same(o_a, "o_a", o_a.shape, torch.float32)
     r = o_a.shape[0] if rows is None else int(rows)
-    stride = lse_a.shape[-1] if lse_stride is None else int(lse_stride)
+    stride = lse_a.stride(0) if lse_stride is None else int(lse_stride)
+    if not 1 <= r <= o_a.shape[0]:
+        raise ValueError(f"rows = {r} outside [1, {o_a.shape[0]}]")
+    # lse operands: [h, >= rows] views with unit column stride whose rows are
+    # lse_stride elements apart (a column slice of a [h, T] tensor is fine)
+    for t, nm in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse_out, "lse_out")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.shape[0] != o_a.shape[1] or t.shape[1] < r:
+            raise ValueError(f"{nm} must be [h = {o_a.shape[1]}, >= rows = {r}]")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be {torch.float32}, got {t.dtype}")
+        if t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) != stride):
+            raise ValueError(f"{nm} must have unit column stride and row stride lse_stride = {stride}")
     for t, nm in ((o_a, "o_a"), (o_b, "o_b"), (o_out, "o_out")):
         _dev(t, nm, torch.float32)
     for t, nm in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse_out, "lse_out")):
-        if t.dtype != torch.float32 or not t.is_cuda:
+        if not t.is_cuda:
             raise TypeError(f"{nm} must be a float32 device tensor")
     check(lib().segattn_merge(r, o_a.shape[1], o_a.shape[2], stride, ctypes.c_void_p(o_a.data_ptr()),
                               ctypes.c_void_p(lse_a.data_ptr()), ctypes.c_void_p(o_b.data_ptr()),
@@ -187,7 +231,14 @@ def segattn_bwd_workspace(shape, items):
 
 def segattn_bwd_preprocess(q, k, o, do, items, workspace, *, scale=None, stream=None):
     shape = make_shape(q, k, scale)
+    _same(o, "o", q.shape, dtypes=(torch.bfloat16, torch.float32))
+    _same(do, "do", q.shape, q.dtype)
     arr, p, n = _items_arg(items)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a tensor")
+    need = segattn_bwd_workspace(shape, arr)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace too small: {need} bytes needed")
     check(lib().segattn_bwd_preprocess(ctypes.byref(shape), _dev(o, "o"), _DTYPE_CODE[o.dtype], _dev(do, "do"),
                                        p, n, _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
 
@@ -197,14 +248,22 @@ def segattn_bwd(q, k, v, o, lse, do, items, *, scale=None, dq=None, dk=None, dv=
     """Gradients (dq, dk, dv) of sum(do * o); allocated (zero-filled) when
     not given, in g_dtype (default q's dtype; float32 with accumulate)."""
     shape = make_shape(q, k, scale)
+    _check_kv(q, k, v)
+    _check_stats(q, o, lse)
+    _same(do, "do", q.shape, q.dtype)
     arr, p, n = _items_arg(items)
-    gd = g_dtype or (torch.float32 if accumulate else q.dtype)
+    gd = g_dtype or (dq.dtype if dq is not None else (torch.float32 if accumulate else q.dtype))
     if dq is None:
         dq = torch.zeros(q.shape, dtype=gd, device=q.device)
     if dk is None:
         dk = torch.zeros(k.shape, dtype=gd, device=q.device)
     if dv is None:
         dv = torch.zeros(v.shape, dtype=gd, device=q.device)
+    _same(dq, "dq", q.shape, dtypes=(torch.bfloat16, torch.float32))
+    _same(dk, "dk", k.shape, dq.dtype)
+    _same(dv, "dv", k.shape, dq.dtype)
+    if accumulate and dq.dtype != torch.float32:
+        raise TypeError("accumulate=True needs float32 gradients")
     ws = _workspace(segattn_bwd_workspace(shape, arr), q.device, workspace)
     flags = (SEGATTN_ACCUMULATE if accumulate else 0) | (SEGATTN_D_READY if d_ready else 0)
     check(lib().segattn_bwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
