@@ -15,6 +15,7 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -42,15 +43,14 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="segattn_build_") as tmp:
-        objs = []
-        for src in HIP_SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            _run([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
-            objs.append(obj)
-        for src in CPP_SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            _run([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
-            objs.append(obj)
+        cmds = [[HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src),
+                 "-o", os.path.join(tmp, src + ".o")] for src in HIP_SOURCES]
+        cmds += [[HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src),
+                  "-o", os.path.join(tmp, src + ".o")] for src in CPP_SOURCES]
+        objs = [c[-1] for c in cmds]
+        # one compiler process per translation unit, all at once
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            list(ex.map(_run, cmds))
         tmp_lib = LIB + ".tmp"
         _run([HIPCC, "-shared", "-fPIC", *DEVICE_FLAGS, *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
