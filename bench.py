@@ -41,6 +41,13 @@ Throughput is algorithmic: 14 * d * pairs * Hq FLOP per step (forward
 pairs; masked and recomputed work is not counted), divided by the GPU time of
 the timed steps (HIP events on the stream the library launches on).
 
+With the default workload the line also carries "other_configs": one
+warm-up and one timed step of each other long-sequence workload (131072-token
+ring, 262144-token varlen batch at its typical and tail seeds, 1048576-token
+layer), and "device" with the compute-unit count; the GPU clock is read with
+amd-smi in the middle of the million-token step.  "cpu_baseline" carries the
+GPU result's errors against the oracle result it times ("gpu_parity").
+
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with an
 error message.
 """
@@ -102,6 +109,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="seg32k", choices=["seg32k", "ring128k", "varlen256k", "varlen256k_tail", "seg1m"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the one-step timings of the ring, varlen and million-token workloads")
     p.add_argument("--no-hbm-kernels", action="store_true",
                    help="skip the separate merge / D-reduction bandwidth measurements")
     p.add_argument("--cpu-tokens", type=int, default=32768,
@@ -237,8 +246,8 @@ def cpu_baseline(W, synth, tokens, heads=2):
     do = synth.to_numpy_f32(W.do[:tok, :hh])
     scale = 1.0 / math.sqrt(W.d)
     t0 = time.perf_counter()
-    oracle.attention_fwd(q, k, v, None, scale)
-    oracle.attention_bwd(q, k, v, do, None, scale)
+    ro, rl = oracle.attention_fwd(q, k, v, None, scale)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, None, scale)
     dt = time.perf_counter() - t0
     flops = 14 * W.d * (tok * (tok + 1) // 2) * hh
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -251,9 +260,28 @@ def cpu_baseline(W, synth, tokens, heads=2):
                     break
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 NumPy oracle, forward+backward of {hh} head(s) over the first {tok} tokens "
-                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s; cpu: {model}"}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"float64 NumPy oracle, forward+backward of {hh} head(s) over the first {tok} tokens "
+                     f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s; cpu: {model}"}
+    # The same oracle result against the GPU's outputs of the last timed step
+    # (max-abs and relative L2 per tensor).  Query rows of a causal prefix see
+    # only keys of the prefix, so O, LSE and dQ compare whenever the sample
+    # starts a single sequence; dK and dV need every later row, so they
+    # compare only when the sample is the whole sequence.
+    if W.cu is None:
+        def err(got, ref):
+            g = np.asarray(got, np.float64)
+            d_ = g - ref
+            return {"max_abs": float(np.abs(d_).max()), "rel_l2": float(np.linalg.norm(d_) / np.linalg.norm(ref))}
+        par = {"O": err(synth.to_numpy_f32(W.o[:tok, :hh]), ro), "LSE": err(synth.to_numpy_f32(W.lse[:hh, :tok]), rl),
+               "dQ": err(synth.to_numpy_f32(W.dq[:tok, :hh]), rq)}
+        if tok == W.T:
+            par["dK"] = err(synth.to_numpy_f32(W.dk[:tok, :hk]), rk)
+            par["dV"] = err(synth.to_numpy_f32(W.dv[:tok, :hk]), rv)
+        out["gpu_parity"] = {"heads": hh, "tokens": tok,
+                             "bars": {"O, LSE": "max_abs <= 1e-2, rel_l2 <= 5e-3", "dQ, dK, dV": "rel_l2 <= 1e-2"},
+                             **par}
+    return out
 
 
 def hbm_kernels(torch, sa, W):
@@ -596,6 +624,66 @@ def offload_bench(torch, sa, synth, reps=5):
         "grads_bit_identical": bool(same)}), flush=True)
 
 
+def smi_clocks():
+    """Current and maximum gfx clocks of GPU 0 per XCD (MHz), as amd-smi
+    reports them right now, or the error text."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+        clk = json.loads(r.stdout)["gpu_data"][0]["clock"]
+        gfx = sorted((k_ for k_ in clk if k_.startswith("gfx_")), key=lambda x: int(x.split("_")[1]))
+        return {"gfx_mhz": [clk[k_]["clk"]["value"] for k_ in gfx],
+                "max_mhz": max(clk[k_]["max_clk"]["value"] for k_ in gfx)}
+    except Exception as e:  # noqa: BLE001 -- reported, never fatal
+        return {"error": str(e)[:200]}
+
+
+def device_info(torch):
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count,
+            "peak_assumes": "256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU (AMD's published MI355X peak engine clock)"}
+
+
+def other_configs(torch, sa, synth, names, clock_probe="seg1m"):
+    """One warm-up and one timed step of each further workload (the 131072-
+    token ring, the varlen batch at its typical and tail seeds, the million-
+    token layer), each with its own breakdown, TFLOP/s, % of peak and the
+    backward kernel's roofline fraction.  While the timed step of
+    `clock_probe` runs (about 40 s of MFMA work) the GPU clock is read with
+    amd-smi, which gives the sustained clock under this load."""
+    E = torch.cuda.Event
+    res = {}
+    for name in names:
+        W = Workload(name, torch, sa, synth)
+        run_step(W, torch)
+        torch.cuda.synchronize()
+        ev = [E(enable_timing=True) for _ in range(4)]
+        run_step(W, torch, ev)
+        clocks = None
+        if name == clock_probe:
+            time.sleep(20.0)  # the step's kernels are queued; sample inside the backward
+            clocks = smi_clocks()
+        torch.cuda.synchronize()
+        tot = ev[0].elapsed_time(ev[3])
+        f, pre, b = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])
+        tf = (W.flops_fwd + W.flops_bwd) / (tot * 1e-3) / 1e12
+        bk = W.flops_bwd / (b * 1e-3) / 1e12
+        fk = W.flops_fwd / (f * 1e-3) / 1e12
+        res[W.w["name"]] = {
+            "tokens": W.T, "q_heads": W.hq, "kv_heads": W.hkv, "items": int(len(W.items)),
+            "longest_sequence": int(max(W.lengths)), "visible_pairs_per_head": int(W.pairs),
+            "warmup": 1, "steps": 1, "ms_per_step": round(tot, 3),
+            "breakdown_ms": {"fwd": round(f, 3), "bwd_preprocess": round(pre, 3), "bwd": round(b, 3)},
+            "tflops": round(tf, 1), "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "bwd_kernel_frac": round(bk / PEAK_BF16_TFLOPS, 4), "fwd_kernel_frac": round(fk / PEAK_BF16_TFLOPS, 4)}
+        if clocks is not None:
+            res[W.w["name"]]["clocks_mid_step"] = clocks
+        print(f"# {W.w['name']}: {tot:.1f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del W
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -675,10 +763,16 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(tag, W.w["name"])},
     }
+    out["device"] = device_info(torch)
     if not args.no_hbm_kernels:
         out["hbm_kernels"] = hbm_kernels(torch, sa, W)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, synth, args.cpu_tokens)
+    if not args.no_other_configs and args.workload == "seg32k":
+        del W
+        torch.cuda.empty_cache()
+        out["other_configs"] = other_configs(torch, sa, synth,
+                                             ["ring128k", "varlen256k", "varlen256k_tail", "seg1m"])
     print(json.dumps(out), flush=True)
 
 

@@ -80,9 +80,11 @@ def _softmax_rows(z):
     return p, lse[:, 0]
 
 
-def attention_fwd(q, k, v, cu_seqlens=None, scale=None):
+def attention_fwd(q, k, v, cu_seqlens=None, scale=None, progress=None):
     """Unsegmented causal attention over each packed sequence.
-    Returns (O [T,Hq,d] float64, LSE [Hq,T] float64)."""
+    Returns (O [T,Hq,d] float64, LSE [Hq,T] float64).  progress, if given,
+    is called with (rows done, rows in all) after each block of query rows
+    (it only reports; nothing it returns is used)."""
     _check(q, k, v)
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -104,6 +106,8 @@ def attention_fwd(q, k, v, cu_seqlens=None, scale=None):
                 p, l_ = _softmax_rows(z)
                 o[a + r0:a + r1, h] = p @ V[:r1]
                 lse[h, a + r0:a + r1] = l_
+                if progress is not None:
+                    progress(h * T + a + r1, hq * T)
     return o, lse
 
 
@@ -174,9 +178,10 @@ def segmented_fwd(q, k, v, items, scale=None):
     return o, lse
 
 
-def attention_bwd(q, k, v, do, cu_seqlens=None, scale=None):
+def attention_bwd(q, k, v, do, cu_seqlens=None, scale=None, progress=None):
     """Gradients of f = sum(dO * O) for unsegmented causal attention over
-    each packed sequence.  Returns (dq, dk, dv), float64."""
+    each packed sequence.  Returns (dq, dk, dv), float64.  progress as in
+    attention_fwd."""
     _check(q, k, v)
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -205,6 +210,8 @@ def attention_bwd(q, k, v, do, cu_seqlens=None, scale=None):
                 dS = P * (dP - D)
                 dq[a + r0:a + r1, h] += scale * (dS @ K[:r1])
                 dk[a:a + r1, g] += scale * (dS.T @ Q[r0:r1])
+                if progress is not None:
+                    progress(h * T + a + r1, hq * T)
     return dq, dk, dv
 
 

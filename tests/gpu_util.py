@@ -69,3 +69,21 @@ def ring_steps(items):
             return steps
         steps.append(np.array(st, np.int64))
         s += 1
+
+
+class Progress:
+    """Progress callback for the oracle's long loops: prints the rows done
+    at most every `every_s` seconds (a full-size oracle head runs for
+    minutes)."""
+
+    def __init__(self, what, every_s=20.0):
+        import time
+        self.what, self.every, self.t0 = what, every_s, time.perf_counter()
+        self.last = self.t0
+
+    def __call__(self, done, total):
+        import time
+        now = time.perf_counter()
+        if now - self.last >= self.every or done == total:
+            self.last = now
+            say(f"  {self.what}: {done}/{total} rows, {now - self.t0:.0f} s")

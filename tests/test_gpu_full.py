@@ -31,7 +31,7 @@ import torch
 
 import oracle
 import segmented_causal_attention_amd as sa
-from gpu_util import assert_close_g, assert_close_o, ring_steps, say, segments
+from gpu_util import Progress, assert_close_g, assert_close_o, ring_steps, say, segments
 from synthetic_inputs import WORKLOADS, cu_seqlens, gen_tensors, lognormal_lengths, tail_seed, to_numpy_f32
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +102,24 @@ def _check_invariants(do, dk, dv, cu, hq, hkv, what):
     assert rk < 1e-2 and rv < 1e-2, (rk, rv)
 
 
+def _whole_heads(q, k, v, do, o, lse, dq, dk, dv, heads, scale, what):
+    """Every entry of O, LSE, dQ, dK and dV of whole heads (one causal
+    sequence, MHA: KV head = query head) against the float64 oracle run on
+    those heads alone -- the unsegmented definition over all rows and keys,
+    so the early keys, which gather gradient from every later segment and
+    ring block, are compared entry by entry too."""
+    hs = list(heads)
+    h32 = [_f32(x[:, hs]) for x in (q, k, v, do)]
+    ro, rl = oracle.attention_fwd(h32[0], h32[1], h32[2], None, scale, progress=Progress(f"{what} oracle fwd"))
+    rq, rk, rv = oracle.attention_bwd(*h32, None, scale, progress=Progress(f"{what} oracle bwd"))
+    for i, h in enumerate(hs):
+        assert_close_o(o[:, h].float(), ro[:, i], f"{what} whole head {h} O")
+        assert_close_o(lse[h], rl[i], f"{what} whole head {h} LSE")
+        assert_close_g(dq[:, h].float(), rq[:, i], f"{what} whole head {h} dQ")
+        assert_close_g(dk[:, h].float(), rk[:, i], f"{what} whole head {h} dK")
+        assert_close_g(dv[:, h].float(), rv[:, i], f"{what} whole head {h} dV")
+
+
 def _bwd(q, k, v, o, lse, do, items):
     rev = np.ascontiguousarray(np.asarray(items)[::-1])
     return sa.segattn_bwd(q, k, v, o, lse, do, rev)
@@ -109,6 +127,7 @@ def _bwd(q, k, v, o, lse, do, items):
 
 # ------------------------------------------------------------ ring workload
 
+@pytest.mark.timeout(900)
 def test_ring_131072_full_size():
     w = WORKLOADS["ring128k"]
     S, H, d, N, B = w["S"], w["hq"], w["d"], w["N"], w["block"]
@@ -134,6 +153,27 @@ def test_ring_131072_full_size():
         _check_rows(q, k, v, do, o, lse, dq, 0, S, h, h, rows, scale, "ring")
     _check_tail_keys(q, k, v, do, dk, dv, 0, S, 0, H, H, 48, scale, "ring")
     _check_invariants(do, dk, dv, [0, S], H, H, "ring")
+    # one whole head through all 8 ring blocks (about 2.5 min of CPU)
+    _whole_heads(q, k, v, do, o, lse, dq, dk, dv, [7], scale, "ring")
+
+
+# ------------------------------------------------------- 32768-token layer
+
+def test_seg_32768_two_whole_heads():
+    """The default benchmark workload (32768 tokens, 32 heads, 8 FLOPs-
+    balanced segments, bf16 O and gradients, as the benchmark runs it):
+    two whole heads compared entry by entry."""
+    w = WORKLOADS["seg32k"]
+    S, H, d, N = w["S"], w["hq"], w["d"], w["N"]
+    scale = 1 / math.sqrt(d)
+    say(f"case seg32k whole heads seed={w['seed']} S={S} H={H} d={d} N={N}")
+    t = gen_tensors(w["seed"], S, H, H, d, device=DEV)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    items = segments(sa.segattn_partition(S, N))
+    o, lse = sa.segattn_fwd(q, k, v, items)
+    dq, dk, dv = _bwd(q, k, v, o, lse, do, items)
+    torch.cuda.synchronize()
+    _whole_heads(q, k, v, do, o, lse, dq, dk, dv, [0, H - 1], scale, "seg32k")
 
 
 # ------------------------------------------------------ variable-length batch
