@@ -33,7 +33,9 @@
  *     passed as void*, NULL = the default stream).  The library never
  *     synchronises, never allocates or frees memory, keeps no pointer after
  *     a call returns and has no global mutable state except the thread-local
- *     error string.  Device faults surface at the caller's next sync.
+ *     error string and the per-device scratch of segattn_bwd_noalloc (its
+ *     comment says how calls share it).  Device faults surface at the
+ *     caller's next sync.
  *   - Ownership: the caller owns every buffer.  "device" pointers are HIP
  *     device memory, "host" pointers ordinary host memory.
  *   - Layouts (contiguous, strides implied, 16-byte aligned device pointers):
@@ -240,6 +242,30 @@ int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const 
                 const void *o, int32_t o_dtype, const float *lse, const void *d_o,
                 const segattn_item *items, int32_t n_items, void *dq, void *dk, void *dv,
                 int32_t g_dtype, uint32_t flags, void *workspace, size_t ws_bytes, void *stream);
+
+/* Maximum scratch of segattn_bwd_noalloc: 64 MiB per device. */
+#define SEGATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* segattn_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, meaning and results as segattn_bwd, without the
+ * workspace: D and the plan tables go into a 64 MiB array of the library's
+ * own device memory (SEGATTN_NOALLOC_SCRATCH_BYTES), which every GPU the
+ * library runs on holds until the process ends.  The call allocates
+ * nothing.  It uses the scratch of the CALLER'S CURRENT DEVICE (the stream
+ * must belong to it).  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give wrong results.  Nothing in the scratch has to start at zero (D and
+ * the tables are written before they are read).  SEGATTN_D_READY is not
+ * accepted (D is always computed).  A call whose scratch need --
+ * segattn_bwd_workspace bytes, about 4 * hq * tokens for D -- exceeds the
+ * maximum returns E_WORKSPACE before launching anything.
+ * Errors: as segattn_bwd, plus E_WORKSPACE for a too-large call. */
+int segattn_bwd_noalloc(const segattn_shape *shape, const void *q, const void *k, const void *v, const void *o,
+                        int32_t o_dtype, const float *lse, const void *d_o, const segattn_item *items,
+                        int32_t n_items, void *dq, void *dk, void *dv, int32_t g_dtype, uint32_t flags,
+                        void *stream);
 
 /* ---------------------------------------------------------------- offload
  * Moving a subsequence's backward-only activations to host memory while the

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SegattnError,
     make_shape,
     segattn_bwd,
+    segattn_bwd_noalloc,
     segattn_bwd_preprocess,
     segattn_bwd_workspace,
     segattn_chunk_varlen,

@@ -29,6 +29,8 @@ SEGATTN_D_READY = 4
 SEGATTN_D2H = 0
 SEGATTN_H2D = 1
 
+SEGATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 # Every symbol declared in include/segattn.h.
 EXPORTS = (
     "segattn_partition",
@@ -44,6 +46,7 @@ EXPORTS = (
     "segattn_copy_rows",
     "segattn_stream_order",
     "segattn_bwd",
+    "segattn_bwd_noalloc",
     "segattn_status_string",
     "segattn_last_error",
     "segattn_version",
@@ -95,6 +98,8 @@ def lib():
     L.segattn_bwd_preprocess.argtypes = [P(Shape), vp, i32, vp, P(Item), i32, vp, sz, vp]
     L.segattn_bwd.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, P(Item), i32, vp, vp, vp, i32,
                               ctypes.c_uint32, vp, sz, vp]
+    L.segattn_bwd_noalloc.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, P(Item), i32, vp, vp, vp, i32,
+                                      ctypes.c_uint32, vp]
     f64 = ctypes.c_double
     L.segattn_offload_plan.argtypes = [P(i64), P(i64), i32, f64, P(f64), P(i64), P(f64), P(f64)]
     L.segattn_copy_rows.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]

@@ -273,6 +273,30 @@ def segattn_bwd(q, k, v, o, lse, do, items, *, scale=None, dq=None, dk=None, dv=
     return dq, dk, dv
 
 
+def segattn_bwd_noalloc(q, k, v, o, lse, do, items, dq, dk, dv, *, scale=None, accumulate=False, stream=None):
+    """segattn_bwd without a workspace: the library keeps D and its tables in
+    its own per-device scratch (SEGATTN_NOALLOC_SCRATCH_BYTES), so the C call
+    allocates nothing.  dq, dk, dv must be given (this wrapper allocates
+    nothing either).  Calls that overlap on one GPU share that scratch and
+    race."""
+    shape = make_shape(q, k, scale)
+    _check_kv(q, k, v)
+    _check_stats(q, o, lse)
+    _same(do, "do", q.shape, q.dtype)
+    _same(dq, "dq", q.shape, dtypes=(torch.bfloat16, torch.float32))
+    _same(dk, "dk", k.shape, dq.dtype)
+    _same(dv, "dv", k.shape, dq.dtype)
+    if accumulate and dq.dtype != torch.float32:
+        raise TypeError("accumulate=True needs float32 gradients")
+    arr, p, n = _items_arg(items)
+    flags = SEGATTN_ACCUMULATE if accumulate else 0
+    check(lib().segattn_bwd_noalloc(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                                    _DTYPE_CODE[o.dtype], _dev(lse, "lse", torch.float32), _dev(do, "do"), p, n,
+                                    _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _DTYPE_CODE[dq.dtype], flags,
+                                    _stream(stream)))
+    return dq, dk, dv
+
+
 # ------------------------------------------------------------------ offload
 
 def segattn_offload_plan(rows, row_bytes, threshold_bytes):

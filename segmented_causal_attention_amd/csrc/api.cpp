@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -376,12 +377,12 @@ extern "C" int segattn_bwd_preprocess(const segattn_shape *shape, const void *o,
   return SEGATTN_OK;
 }
 
-extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const void *v, const void *o,
-                           int32_t o_dtype, const float *lse, const void *d_o, const segattn_item *items,
-                           int32_t n_items, void *dq, void *dk, void *dv, int32_t g_dtype, uint32_t flags,
-                           void *workspace, size_t ws_bytes, void *stream) {
-  clear_error();
-  static const char *fn = "segattn_bwd";
+namespace {
+
+// Everything segattn_bwd checks except the workspace; builds the plan.
+int bwd_check(const char *fn, const segattn_shape *shape, const void *q, const void *k, const void *v,
+              const void *o, int32_t o_dtype, const float *lse, const void *d_o, const segattn_item *items,
+              int32_t n_items, void *dq, void *dk, void *dv, int32_t g_dtype, uint32_t flags, BwdPlan &plan) {
   if (int rc = check_shape(shape, fn)) return rc;
   const void *ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
   const char *names[] = {"q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv"};
@@ -393,17 +394,21 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   if ((flags & SEGATTN_ACCUMULATE) && g_dtype != SEGATTN_F32)
     return fail(SEGATTN_E_INVALID, "%s: SEGATTN_ACCUMULATE needs fp32 gradients", fn);
   if (int rc = check_items(shape, items, n_items, fn)) return rc;
-  BwdPlan plan;
   if (int rc = build_bwd_plan(items, n_items, plan, fn)) return rc;
-  const size_t need = bwd_ws_bytes(shape, plan);
-  if (!workspace || ws_bytes < need)
-    return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
-  if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
   const int64_t kv_blocks = (int64_t)plan.n_kv_units * shape->hkv;
   const int64_t kv_pad = (kv_blocks + 7) / 8 * 8;
   if (kv_pad + (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
+  return SEGATTN_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// Table upload, D (unless SEGATTN_D_READY) and the backward kernel, with D
+// and the tables in `workspace` (at least bwd_ws_bytes(shape, plan) bytes).
+int bwd_launch(const char *fn, const segattn_shape *shape, const void *q, const void *k, const void *v,
+               const void *o, int32_t o_dtype, const float *lse, const void *d_o, int32_t n_items, void *dq,
+               void *dk, void *dv, int32_t g_dtype, uint32_t flags, const BwdPlan &plan, void *workspace,
+               hipStream_t s) {
+  const int64_t kv_blocks = (int64_t)plan.n_kv_units * shape->hkv;
+  const int64_t kv_pad = (kv_blocks + 7) / 8 * 8;
   float *delta = static_cast<float *>(workspace);
   BwdTables t;
   if (hipError_t e = upload_bwd_tables(shape, plan, workspace, s, t)) return device_error(e, fn);
@@ -411,8 +416,6 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
     const PreArgs pa = pre_args(shape, plan, o, d_o, delta, t);
     if (hipError_t e = launch_bwd_pre(pa, shape->d, o_dtype, shape->in_dtype, s)) return device_error(e, fn);
   }
-  int32_t *d_items = t.items, *d_kvg = t.kvg, *d_qg = t.qg;
-
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -423,9 +426,9 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.items = d_items;
-  a.kvg = d_kvg;
-  a.qg = d_qg;
+  a.items = t.items;
+  a.kvg = t.kvg;
+  a.qg = t.qg;
   a.n_items = n_items;
   a.n_kvg = (int32_t)(plan.kvg.size() / 4);
   a.n_qg = (int32_t)(plan.qg.size() / 4);
@@ -441,6 +444,79 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
   a.accumulate = (flags & SEGATTN_ACCUMULATE) ? 1 : 0;
   if (hipError_t e = launch_bwd(a, shape->d, shape->in_dtype, g_dtype, s)) return device_error(e, fn);
   return SEGATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void *k, const void *v, const void *o,
+                           int32_t o_dtype, const float *lse, const void *d_o, const segattn_item *items,
+                           int32_t n_items, void *dq, void *dk, void *dv, int32_t g_dtype, uint32_t flags,
+                           void *workspace, size_t ws_bytes, void *stream) {
+  clear_error();
+  static const char *fn = "segattn_bwd";
+  BwdPlan plan;
+  if (int rc = bwd_check(fn, shape, q, k, v, o, o_dtype, lse, d_o, items, n_items, dq, dk, dv, g_dtype, flags, plan))
+    return rc;
+  const size_t need = bwd_ws_bytes(shape, plan);
+  if (!workspace || ws_bytes < need)
+    return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
+  return bwd_launch(fn, shape, q, k, v, o, o_dtype, lse, d_o, n_items, dq, dk, dv, g_dtype, flags, plan, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------- backward, no allocation
+// The backward's scratch (D and the plan tables) in a file-scope device
+// array instead of a caller's workspace.  Host code never passes the array's
+// name to a kernel (on the host it only names a stand-in): the array's
+// device address is taken once per device with hipGetSymbolAddress, with
+// that device current, and kept in scratch_addr[].
+static __device__ __align__(256) char scratch[SEGATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices] = {};
+
+int scratch_of_current_device(const char *fn, void **out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return device_error(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(SEGATTN_E_DEVICE, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return device_error(e, fn);
+    if (!p) return fail(SEGATTN_E_DEVICE, "%s: no device address for the scratch array", fn);
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return SEGATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int segattn_bwd_noalloc(const segattn_shape *shape, const void *q, const void *k, const void *v,
+                                   const void *o, int32_t o_dtype, const float *lse, const void *d_o,
+                                   const segattn_item *items, int32_t n_items, void *dq, void *dk, void *dv,
+                                   int32_t g_dtype, uint32_t flags, void *stream) {
+  clear_error();
+  static const char *fn = "segattn_bwd_noalloc";
+  if (flags & SEGATTN_D_READY)
+    return fail(SEGATTN_E_INVALID, "%s: SEGATTN_D_READY is not available (D lives in the library's scratch)", fn);
+  BwdPlan plan;
+  if (int rc = bwd_check(fn, shape, q, k, v, o, o_dtype, lse, d_o, items, n_items, dq, dk, dv, g_dtype, flags, plan))
+    return rc;
+  const size_t need = bwd_ws_bytes(shape, plan);
+  if (need > (size_t)SEGATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(SEGATTN_E_WORKSPACE,
+                "%s: this call needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                "(use segattn_bwd with a workspace)",
+                fn, need, (size_t)SEGATTN_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (int rc = scratch_of_current_device(fn, &ws)) return rc;
+  return bwd_launch(fn, shape, q, k, v, o, o_dtype, lse, d_o, n_items, dq, dk, dv, g_dtype, flags, plan, ws,
+                    static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ offload

@@ -240,3 +240,30 @@ def test_merge_argument_errors():
     assert L.segattn_merge(8, 1, 1028, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.SEGATTN_E_UNSUPPORTED
     assert L.segattn_merge(8, 1, 128, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert L.segattn_merge(8, 1, 128, 8, FAKE, ctypes.c_void_p(0x1001), FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_bwd_noalloc_argument_errors():
+    """The no-allocation backward rejects SEGATTN_D_READY and any call whose
+    scratch need exceeds its fixed array, before touching a device."""
+    L = _lib.lib()
+    a, p, n = _items([[0, 0, 8, 0, 8]])
+    s = _shape()
+
+    def call(shape, items, flags=0, g_dtype=1):
+        a_, p_, n_ = _items(items)
+        return L.segattn_bwd_noalloc(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, p_, n_, FAKE, FAKE,
+                                     FAKE, g_dtype, flags, None)
+
+    assert call(s, [[0, 0, 8, 0, 8]], flags=_lib.SEGATTN_D_READY) == _lib.SEGATTN_E_INVALID
+    assert call(s, [[0, 0, 8, 0, 8]], flags=_lib.SEGATTN_ACCUMULATE, g_dtype=0) == _lib.SEGATTN_E_INVALID
+    assert call(s, [[0, 0, 8, 0, 4], [0, 8, 16, 0, 16], [0, 0, 8, 4, 8]]) == _lib.SEGATTN_E_INVALID
+    # D alone: 4 * hq * tokens bytes; 8 heads x 2^22 tokens = 128 MiB > 64 MiB
+    big = _shape(tokens=1 << 22, hq=8, hkv=8)
+    assert call(big, [[0, 0, 1 << 22, 0, 1 << 22]]) == _lib.SEGATTN_E_WORKSPACE
+    msg = L.segattn_last_error().decode()
+    assert "no-allocation" in msg and str(_lib.SEGATTN_NOALLOC_SCRATCH_BYTES) in msg, msg
+    # the workspace the same call would need from segattn_bwd is what does not fit
+    nb = ctypes.c_size_t(0)
+    a2, p2, n2 = _items([[0, 0, 1 << 22, 0, 1 << 22]])
+    assert L.segattn_bwd_workspace(ctypes.byref(big), p2, n2, ctypes.byref(nb)) == 0
+    assert nb.value > _lib.SEGATTN_NOALLOC_SCRATCH_BYTES
