@@ -7,7 +7,6 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -466,31 +465,13 @@ extern "C" int segattn_bwd(const segattn_shape *shape, const void *q, const void
 }
 
 // ------------------------------------------------- backward, no allocation
-// The backward's scratch (D and the plan tables) in a file-scope device
-// array instead of a caller's workspace.  Host code never passes the array's
-// name to a kernel (on the host it only names a stand-in): the array's
-// device address is taken once per device with hipGetSymbolAddress, with
-// that device current, and kept in scratch_addr[].
-static __device__ __align__(256) char scratch[SEGATTN_NOALLOC_SCRATCH_BYTES];
-
+// The backward's scratch (D and the plan tables) in the library's own device
+// array (noalloc_scratch, misc.hip) instead of a caller's workspace.
 namespace {
 
-constexpr int kMaxDevices = 64;
-std::mutex scratch_mu;
-void *scratch_addr[kMaxDevices] = {};
-
 int scratch_of_current_device(const char *fn, void **out) {
-  int dev = -1;
-  if (hipError_t e = hipGetDevice(&dev)) return device_error(e, fn);
-  if (dev < 0 || dev >= kMaxDevices) return fail(SEGATTN_E_DEVICE, "%s: device %d out of range", fn, dev);
-  std::lock_guard<std::mutex> lock(scratch_mu);
-  if (!scratch_addr[dev]) {
-    void *p = nullptr;
-    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return device_error(e, fn);
-    if (!p) return fail(SEGATTN_E_DEVICE, "%s: no device address for the scratch array", fn);
-    scratch_addr[dev] = p;
-  }
-  *out = scratch_addr[dev];
+  if (hipError_t e = noalloc_scratch(out)) return device_error(e, fn);
+  if (!*out) return fail(SEGATTN_E_DEVICE, "%s: no device address for the scratch array", fn);
   return SEGATTN_OK;
 }
 

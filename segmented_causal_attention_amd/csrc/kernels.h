@@ -107,5 +107,8 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 // Copies n int32 words from host memory into dst (device) through kernel
 // arguments: stream-ordered, graph-capturable, no pageable-memory copy.
 hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStream_t s);
+// Device address of the no-allocation scratch array (SEGATTN_NOALLOC_SCRATCH_BYTES)
+// on the current device, looked up once per device.
+hipError_t noalloc_scratch(void **out);
 
 }  // namespace segattn

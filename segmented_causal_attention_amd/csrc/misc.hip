@@ -1,7 +1,11 @@
 // Memory-bound kernels: log-sum-exp merge of partial results, the backward
-// row reduction D = <dO, O>, and the stream-ordered table upload.
+// row reduction D = <dO, O>, and the stream-ordered table upload; and the
+// device array behind segattn_bwd_noalloc.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
+#include "segattn.h"
 
 namespace segattn {
 namespace dev {
@@ -195,6 +199,35 @@ hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hi
   }
 #undef SEGATTN_PRE
   return hipGetLastError();
+}
+
+// ---------------------------------------------------- no-allocation scratch
+// segattn_bwd_noalloc keeps the backward's D and plan tables here instead of
+// in a caller's workspace.  Host code never passes the array's name to a
+// kernel (on the host it only names a stand-in): each device's address of
+// it is taken once with hipGetSymbolAddress, with that device current, and
+// kept in scratch_addr[].
+static __device__ __align__(256) char scratch[SEGATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void **out) {
+  *out = nullptr;
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStream_t s) {

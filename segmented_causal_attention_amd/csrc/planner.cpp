@@ -142,14 +142,16 @@ extern "C" int segattn_partition_varlen(const int64_t *cu, int32_t nseq, int64_t
     needed += lo;
     if (needed > 0x7fffffff) return fail(SEGATTN_E_RANGE, "segattn_partition_varlen: too many items");
   }
-  if (needed > cap) {
-    *n_items = (int32_t)needed;
-    return fail(SEGATTN_E_CAPACITY, "segattn_partition_varlen: %lld items needed, capacity %d",
-                (long long)needed, cap);
-  }
-  // Validate every multi-slice partition before writing anything.
+  // Validate every multi-slice partition (pass 0) before reporting the
+  // capacity or writing anything (pass 1): a capacity query then fails the
+  // same way the call that writes would.
   std::string scratch;
   for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1 && needed > cap) {
+      *n_items = (int32_t)needed;
+      return fail(SEGATTN_E_CAPACITY, "segattn_partition_varlen: %lld items needed, capacity %d",
+                  (long long)needed, cap);
+    }
     int64_t w = 0;
     for (int32_t s = 0; s < nseq; ++s) {
       const int64_t off = cu[s], L = cu[s + 1] - cu[s];

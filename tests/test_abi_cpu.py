@@ -267,3 +267,15 @@ def test_bwd_noalloc_argument_errors():
     a2, p2, n2 = _items([[0, 0, 1 << 22, 0, 1 << 22]])
     assert L.segattn_bwd_workspace(ctypes.byref(big), p2, n2, ctypes.byref(nb)) == 0
     assert nb.value > _lib.SEGATTN_NOALLOC_SCRATCH_BYTES
+
+
+def test_varlen_capacity_query_fails_like_the_call():
+    """A slice cap so small that the balanced partition of a sequence would
+    hold an empty slice is E_RANGE for the capacity query as well, not a
+    count that the writing call then refuses."""
+    L = _lib.lib()
+    cu = np.array([0, 62210], np.int64)
+    n = ctypes.c_int32(0)
+    st = L.segattn_partition_varlen(cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1, 2, None, 0,
+                                    ctypes.byref(n))
+    assert st == _lib.SEGATTN_E_RANGE, (st, n.value)
