@@ -20,7 +20,9 @@ plan).
 
 --latency-small times the small oracle-identity case (1024 tokens, one head,
 d = 64, fp32 inputs, 4 FLOPs-balanced segments, forward only), which is
-launch-bound: GPU time and host wall time per call, one JSON line.
+launch-bound: per call, with and without key pieces (SEGATTN_SPLIT_KEYS),
+the GPU time and host wall time of back-to-back eager calls and the GPU time
+of the call replayed from a captured HIP graph; one JSON line.
 
 --offload measures sequence-aware offloading (SPPO sections 5.1-5.2) on the
 default workload, and prints one JSON line with the result.  The forward and
@@ -458,12 +460,18 @@ def chunking_bench(torch, sa, synth, reps=3, token_cap=16384, ks=(1, 2, 3, 4, 5)
                {"K": K, "token_cap": token_cap, "final_time_threshold": tt})
 
 
-def c1_latency(torch, sa, synth, calls=500, warmup=50):
+def c1_latency(torch, sa, synth, calls=500, warmup=50, per_graph=50, replays=10):
     """Per-call latency of the forward over the 1024-token, one-head, d = 64
     fp32 workload in 4 FLOPs-balanced segments (one segattn_fwd call with 4
-    items).  GPU time: HIP events around `calls` back-to-back calls on the
-    launch stream.  Host time: wall clock of the same calls, including the
-    host-side checks, table upload and launch, until the stream drains."""
+    items), with and without SEGATTN_SPLIT_KEYS (the query tiles' key walks
+    cut into pieces on separate workgroups and merged by log-sum-exp).
+      eager: HIP events around `calls` back-to-back calls on the launch
+        stream, and the host wall clock of the same calls (host-side checks,
+        planning, table upload and launch included) until the stream drains;
+      graph_replay: the same call captured `per_graph` times into one HIP
+        graph (torch.cuda.graph), replayed `replays` times: the GPU's time
+        per call without the host path.  Every replay's outputs are checked
+        bit for bit against the eager call's."""
     w = synth.WORKLOADS["seg1k_fp32"]
     S, N, d = w["S"], w["N"], w["d"]
     t = synth.gen_tensors(w["seed"], S, w["hq"], w["hkv"], d, dtype="fp32", device="cuda")
@@ -473,23 +481,65 @@ def c1_latency(torch, sa, synth, calls=500, warmup=50):
     o = torch.empty((S, w["hq"], d), dtype=torch.float32, device="cuda")
     lse = torch.empty((w["hq"], S), dtype=torch.float32, device="cuda")
     fws = torch.empty(max(sa.segattn_fwd_workspace(sa.make_shape(q, k), items), 16), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(calls):
-        sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_us = e0.elapsed_time(e1) * 1e3 / calls
     flops = 4 * d * visible_pairs([S]) * w["hq"]
+    E = torch.cuda.Event
+
+    def call(split, stream=None):
+        sa.segattn_fwd(q, k, v, items, o=o, lse=lse, workspace=fws, split_keys=split, stream=stream)
+
+    def eager(split):
+        for _ in range(warmup):
+            call(split)
+        torch.cuda.synchronize()
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(calls):
+            call(split)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) * 1e3 / calls, wall * 1e6 / calls
+
+    def graph(split):
+        call(split)
+        torch.cuda.synchronize()
+        ref_o, ref_l = o.clone(), lse.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                call(split)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                call(split)
+        times, same = [], True
+        for _ in range(replays):
+            o.fill_(float("nan"))  # eager work between replays; every replay must rewrite the outputs
+            lse.fill_(float("nan"))
+            e0, e1 = E(enable_timing=True), E(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / per_graph)
+            same = same and torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+        del g
+        return float(np.median(times)), bool(same)
+
+    res = {}
+    for split in (False, True):
+        gpu_us, host_us = eager(split)
+        g_us, same = graph(split)
+        res["split" if split else "unsplit"] = {
+            "gpu_us_per_call": round(gpu_us, 2), "host_us_per_call": round(host_us, 2),
+            "graph_replay_us_per_call": round(g_us, 2), "graph_replays_bit_identical": same,
+            "tflops_at_graph_time": round(flops / (g_us * 1e-6) / 1e12, 3)}
     print(json.dumps({"latency": "fwd", "workload": w["name"], "segments": N, "bounds": b, "calls": calls,
-                      "gpu_us_per_call": round(gpu_us, 2), "host_us_per_call": round(wall * 1e6 / calls, 2),
-                      "flops_per_call": flops, "tflops_at_gpu_time": round(flops / (gpu_us * 1e-6) / 1e12, 3)}),
-          flush=True)
+                      "flops_per_call": flops, **res}), flush=True)
 
 
 def offload_bench(torch, sa, synth, reps=5):

@@ -73,6 +73,7 @@ extern "C" {
 #define SEGATTN_MERGE_INTO  1u /* fwd: merge the new partial into the fp32 (O, LSE) already in o/lse */
 #define SEGATTN_ACCUMULATE  2u /* bwd: dq/dk/dv are fp32 accumulators; results are added to them */
 #define SEGATTN_D_READY     4u /* bwd: D was already computed into the workspace by segattn_bwd_preprocess */
+#define SEGATTN_SPLIT_KEYS  8u /* fwd: on a launch too small to fill the GPU, cut long key walks across workgroups */
 
 typedef struct {
   int64_t seq_off, q_lo, q_hi, k_lo, k_hi;
@@ -174,8 +175,17 @@ int segattn_fwd_workspace(const segattn_shape *shape, const segattn_item *items,
  * SEGATTN_F32); lse: device float [hq][tokens].  Only the items' rows are
  * written.  flags: 0, or SEGATTN_MERGE_INTO (o must be F32): the new partial
  * is merged into the (O, LSE) already held in o/lse with the log-sum-exp
- * rule of segattn_merge.  workspace: device, >= segattn_fwd_workspace bytes
- * (may be NULL when that is 0).  stream: hipStream_t.
+ * rule of segattn_merge.  SEGATTN_SPLIT_KEYS (for latency): when the
+ * launch has fewer than 256 (query tile, head) work units, the keys of each
+ * long query tile are cut into up to 8 pieces of at least 2 64-key tiles,
+ * computed by separate workgroups, and a second kernel on the stream
+ * combines them with the same log-sum-exp merge, in piece order (the
+ * segmented-plus-merged evaluation of InfiniPipe section II-A within one
+ * call).  Results are deterministic but rounded differently from the
+ * unsplit walk; without the flag a row's result does not depend on which
+ * other items share the call.  workspace: device, >= segattn_fwd_workspace
+ * bytes, which covers the call with or without the flag.  stream:
+ * hipStream_t.
  * Errors: E_INVALID, E_UNSUPPORTED, E_RANGE, E_WORKSPACE, E_DEVICE. */
 int segattn_fwd(const segattn_shape *shape, const void *q, const void *k, const void *v,
                 const segattn_item *items, int32_t n_items, void *o, int32_t o_dtype, float *lse,

@@ -25,6 +25,7 @@ SEGATTN_F32 = 1
 SEGATTN_MERGE_INTO = 1
 SEGATTN_ACCUMULATE = 2
 SEGATTN_D_READY = 4
+SEGATTN_SPLIT_KEYS = 8
 
 SEGATTN_D2H = 0
 SEGATTN_H2D = 1
@@ -91,14 +92,15 @@ def lib():
     L.segattn_ring_items.argtypes = [P(i64), i32, i64, P(Item), i32, P(i32)]
     L.segattn_chunk_varlen.argtypes = [P(i64), i32, i32, ctypes.c_double, ctypes.c_double, i64, P(Item), P(i32),
                                        i32, P(i32), P(i32), P(ctypes.c_double)]
-    L.segattn_fwd_workspace.argtypes = [P(Shape), P(Item), i32, P(sz)]
-    L.segattn_fwd.argtypes = [P(Shape), vp, vp, vp, P(Item), i32, vp, i32, vp, ctypes.c_uint32, vp, sz, vp]
+    # item tables of the attention calls: host addresses (int) of int64 [n, 5] arrays
+    L.segattn_fwd_workspace.argtypes = [P(Shape), vp, i32, P(sz)]
+    L.segattn_fwd.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, i32, vp, ctypes.c_uint32, vp, sz, vp]
     L.segattn_merge.argtypes = [i64, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp]
-    L.segattn_bwd_workspace.argtypes = [P(Shape), P(Item), i32, P(sz)]
-    L.segattn_bwd_preprocess.argtypes = [P(Shape), vp, i32, vp, P(Item), i32, vp, sz, vp]
-    L.segattn_bwd.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, P(Item), i32, vp, vp, vp, i32,
+    L.segattn_bwd_workspace.argtypes = [P(Shape), vp, i32, P(sz)]
+    L.segattn_bwd_preprocess.argtypes = [P(Shape), vp, i32, vp, vp, i32, vp, sz, vp]
+    L.segattn_bwd.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32,
                               ctypes.c_uint32, vp, sz, vp]
-    L.segattn_bwd_noalloc.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, P(Item), i32, vp, vp, vp, i32,
+    L.segattn_bwd_noalloc.argtypes = [P(Shape), vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32,
                                       ctypes.c_uint32, vp]
     f64 = ctypes.c_double
     L.segattn_offload_plan.argtypes = [P(i64), P(i64), i32, f64, P(f64), P(i64), P(f64), P(f64)]

@@ -18,7 +18,7 @@ import torch
 
 from . import _lib
 from ._lib import (SEGATTN_ACCUMULATE, SEGATTN_BF16, SEGATTN_D_READY, SEGATTN_F32,  # noqa: F401
-                   SEGATTN_MERGE_INTO, Item, SegattnError, Shape, check, lib)
+                   SEGATTN_MERGE_INTO, SEGATTN_SPLIT_KEYS, Item, SegattnError, Shape, check, lib)
 
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _ITEMP = ctypes.POINTER(Item)
@@ -30,35 +30,52 @@ _CODE_DTYPE = {SEGATTN_BF16: torch.bfloat16, SEGATTN_F32: torch.float32}
 # ------------------------------------------------------------------ helpers
 
 def _items_arg(items):
-    a = np.ascontiguousarray(np.asarray(items, dtype=np.int64).reshape(-1, 5))
-    return a, a.ctypes.data_as(_ITEMP), a.shape[0]
+    """(array, pointer, n) of an int64 [n, 5] item table; an array that is
+    already int64, C-contiguous and [n, 5] is passed as it is."""
+    if (type(items) is np.ndarray and items.dtype == np.int64 and items.ndim == 2 and items.shape[1] == 5
+            and items.flags.c_contiguous):
+        a = items
+    else:
+        a = np.ascontiguousarray(np.asarray(items, dtype=np.int64).reshape(-1, 5))
+    return a, a.ctypes.data, a.shape[0]
 
 
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
 def _dev(t, name, dtype=None):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if type(t) is not torch.Tensor or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
+
+
+_SHAPES = {}
 
 
 def make_shape(q, k, scale=None):
-    """segattn_shape for token-major q [T, hq, d] and k [T, hkv, d]."""
-    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
-        raise ValueError("q must be [T, hq, d] and k [T, hkv, d]")
-    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype:
-        raise TypeError("q, k, v must all be bfloat16 or all float32")
-    d = q.shape[2]
-    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    return Shape(q.shape[0], q.shape[1], k.shape[1], d, _DTYPE_CODE[q.dtype], sc)
+    """segattn_shape for token-major q [T, hq, d] and k [T, hkv, d] (one
+    ctypes struct per distinct shape, reused: the library only reads it)."""
+    qs, ks, qd = q.shape, k.shape, q.dtype
+    key = (qs, ks, qd, scale)
+    sh = _SHAPES.get(key)
+    if sh is None:
+        if len(qs) != 3 or len(ks) != 3 or qs[0] != ks[0] or qs[2] != ks[2]:
+            raise ValueError("q must be [T, hq, d] and k [T, hkv, d]")
+        if qd not in _DTYPE_CODE or k.dtype != qd:
+            raise TypeError("q, k, v must all be bfloat16 or all float32")
+        d = qs[2]
+        sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        sh = Shape(qs[0], qs[1], ks[1], d, _DTYPE_CODE[qd], sc)
+        if len(_SHAPES) < 256:
+            _SHAPES[key] = sh
+    return sh
 
 
 def _same(t, name, shape, dtype=None, dtypes=None):
@@ -67,7 +84,7 @@ def _same(t, name, shape, dtype=None, dtypes=None):
     is checked here, before anything is launched."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -82,14 +99,15 @@ def _check_kv(q, k, v):
 def _check_stats(q, o, lse):
     """o [T, hq, d] in bf16 or fp32; lse [hq, T] fp32."""
     _same(o, "o", q.shape, dtypes=(torch.bfloat16, torch.float32))
-    _same(lse, "lse", (q.shape[1], q.shape[0]), torch.float32)
+    _same(lse, "lse", torch.Size((q.shape[1], q.shape[0])), torch.float32)
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace, or a new one of nbytes() bytes.  A given
+    workspace is not measured here: the library checks its size (E_WORKSPACE)
+    before launching anything, which saves a planning pass per call."""
     if workspace is None:
-        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace too small: {nbytes} bytes needed")
+        return torch.empty(max(int(nbytes()), 16), dtype=torch.uint8, device=device)
     return workspace
 
 
@@ -159,10 +177,10 @@ def segattn_fwd_workspace(shape, items):
 
 
 def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, merge_into=False,
-                workspace=None, stream=None):
+                split_keys=False, workspace=None, stream=None):
     """Partial attention of `items` into (o, lse); returns (o, lse).
     New outputs are allocated (o_dtype defaults to q's dtype; lse filled
-    with -inf) when not given."""
+    with -inf) when not given.  split_keys sets SEGATTN_SPLIT_KEYS."""
     shape = make_shape(q, k, scale)
     _check_kv(q, k, v)
     arr, p, n = _items_arg(items)
@@ -173,11 +191,11 @@ def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, m
         lse = torch.full((q.shape[1], q.shape[0]), -math.inf, dtype=torch.float32, device=q.device)
     _check_stats(q, o, lse)
     ocode = _DTYPE_CODE[o.dtype]
-    ws = _workspace(segattn_fwd_workspace(shape, arr), q.device, workspace)
-    flags = SEGATTN_MERGE_INTO if merge_into else 0
+    ws = _workspace(lambda: segattn_fwd_workspace(shape, arr), q.device, workspace)
+    flags = (SEGATTN_MERGE_INTO if merge_into else 0) | (SEGATTN_SPLIT_KEYS if split_keys else 0)
     check(lib().segattn_fwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), p, n,
                             _dev(o, "o"), ocode, _dev(lse, "lse", torch.float32), flags,
-                            _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+                            _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(stream)))
     return o, lse
 
 
@@ -264,12 +282,12 @@ def segattn_bwd(q, k, v, o, lse, do, items, *, scale=None, dq=None, dk=None, dv=
     _same(dv, "dv", k.shape, dq.dtype)
     if accumulate and dq.dtype != torch.float32:
         raise TypeError("accumulate=True needs float32 gradients")
-    ws = _workspace(segattn_bwd_workspace(shape, arr), q.device, workspace)
+    ws = _workspace(lambda: segattn_bwd_workspace(shape, arr), q.device, workspace)
     flags = (SEGATTN_ACCUMULATE if accumulate else 0) | (SEGATTN_D_READY if d_ready else 0)
     check(lib().segattn_bwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
                             _DTYPE_CODE[o.dtype], _dev(lse, "lse", torch.float32), _dev(do, "do"), p, n,
                             _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _DTYPE_CODE[dq.dtype], flags,
-                            _dev(ws, "workspace"), ws.numel(), _stream(stream)))
+                            _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(stream)))
     return dq, dk, dv
 
 

@@ -86,21 +86,68 @@ int device_error(hipError_t e, const char *fn) {
 }
 
 // ------------------------------------------------------------ forward table
-// Items sorted by the cost of their heaviest query tile (keys visible to its
-// last row), heaviest first; each item's tiles run from its last rows to its
-// first, so the whole unit order is heaviest-first for a single sequence.
+// Items sorted by the cost of their heaviest work unit (keys visible to the
+// last row of a query tile, divided among its key pieces), heaviest first;
+// each item's tiles run from its last rows to its first, so the whole unit
+// order is heaviest-first for a single sequence.
+//
+// Key pieces (SEGATTN_SPLIT_KEYS, and only for a launch of fewer than
+// kSplitGrid workgroups): the key tiles of each query tile of an item are
+// cut into P contiguous pieces, one workgroup each, whose partials (O, LSE)
+// a second kernel on the stream combines with the log-sum-exp merge.  P is
+// chosen per item so that a piece keeps at least kMinPieceTiles key tiles,
+// at most kMaxPieces pieces, and the whole launch at most kSplitMaxGrid
+// workgroups.  (Combining them inside the forward -- the last piece to
+// finish, found with an atomic ticket -- needed device-scope fences, which
+// write back and invalidate L2 across the XCDs: 6-12 us per launch, more
+// than the split saved.)
+constexpr int64_t kSplitGrid = 256;
+constexpr int64_t kSplitMaxGrid = 512;
+constexpr int64_t kMinPieceTiles = 2;
+constexpr int64_t kMaxPieces = kFwdMaxPieces;
+
 struct FwdPlan {
   std::vector<int32_t> words;
+  std::vector<int32_t> split_tiles;  // kSplitTileWords per split query tile
   int32_t n_units = 0;
+  int64_t n_parts = 0;  // partial results of split query tiles (per head)
 };
 
-void build_fwd_plan(const segattn_item *items, int32_t n, FwdPlan &p) {
+int64_t fwd_tiles(const segattn_item &it) { return (it.q_hi - it.q_lo + kFwdBM - 1) / kFwdBM; }
+int64_t fwd_key_tiles(const segattn_item &it) {
+  return (std::min(it.k_hi, it.q_hi) - it.k_lo + kFwdBN - 1) / kFwdBN;
+}
+
+// Pieces per item (all 1 unless a split applies).
+std::vector<int64_t> fwd_pieces(const segattn_item *items, int32_t n, int32_t hq, bool split) {
+  std::vector<int64_t> P(n, 1);
+  int64_t grid = 0;
+  for (int32_t i = 0; i < n; ++i) grid += fwd_tiles(items[i]) * hq;
+  if (!split || grid >= kSplitGrid) return P;
+  for (int32_t i = 0; i < n; ++i) P[i] = std::max<int64_t>(1, std::min(kMaxPieces, fwd_key_tiles(items[i]) / kMinPieceTiles));
+  auto total = [&] {
+    int64_t g = 0;
+    for (int32_t i = 0; i < n; ++i) g += fwd_tiles(items[i]) * P[i] * hq;
+    return g;
+  };
+  while (total() > kSplitMaxGrid) {  // take pieces from the item with the most
+    int32_t b = 0;
+    for (int32_t i = 1; i < n; ++i)
+      if (P[i] > P[b]) b = i;
+    if (P[b] == 1) break;
+    --P[b];
+  }
+  return P;
+}
+
+void build_fwd_plan(const segattn_item *items, int32_t n, int32_t hq, bool split, FwdPlan &p) {
+  const std::vector<int64_t> P = fwd_pieces(items, n, hq, split);
   std::vector<int32_t> order(n);
   for (int32_t i = 0; i < n; ++i) order[i] = i;
-  auto cost = [&](int32_t i) { return std::min(items[i].k_hi, items[i].q_hi) - items[i].k_lo; };
+  auto cost = [&](int32_t i) { return (fwd_key_tiles(items[i]) + P[i] - 1) / P[i]; };
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
   p.words.assign((size_t)n * kItemWords, 0);
-  int64_t unit = 0;
+  int64_t unit = 0, part = 0;
   for (int32_t r = 0; r < n; ++r) {
     const segattn_item &it = items[order[r]];
     int32_t *w = &p.words[(size_t)r * kItemWords];
@@ -110,12 +157,38 @@ void build_fwd_plan(const segattn_item *items, int32_t n, FwdPlan &p) {
     w[3] = (int32_t)it.k_lo;
     w[4] = (int32_t)it.k_hi;
     w[5] = (int32_t)unit;
-    unit += (it.q_hi - it.q_lo + kFwdBM - 1) / kFwdBM;
+    w[6] = (int32_t)P[order[r]];
+    w[7] = (int32_t)(P[order[r]] > 1 ? part : 0);
+    unit += fwd_tiles(it) * P[order[r]];
+    if (P[order[r]] > 1) {
+      for (int64_t t = 0; t < fwd_tiles(it); ++t) {  // query tile t: rows [r0, r1), last rows first
+        const int64_t r1 = it.q_hi - t * kFwdBM, r0 = std::max(it.q_lo, r1 - kFwdBM);
+        p.split_tiles.insert(p.split_tiles.end(), {(int32_t)it.seq_off, (int32_t)r0, (int32_t)r1,
+                                                   (int32_t)P[order[r]], (int32_t)(part + t * P[order[r]])});
+      }
+      part += fwd_tiles(it) * P[order[r]];
+    }
   }
   p.n_units = (int32_t)unit;
+  p.n_parts = part;
 }
 
-size_t fwd_ws_bytes(int32_t n) { return align_up((size_t)n * kItemWords * sizeof(int32_t)); }
+// Workspace: the item table and the split-tile table (one upload), then
+// (split plans only) the partial LSEs [part][head][kFwdBM] and the partial
+// O [part][head][kFwdBM][d] (fp32).
+struct FwdLayout {
+  size_t split_tiles = 0, part_lse = 0, part_o = 0, bytes = 0;
+};
+
+FwdLayout fwd_layout(int32_t n, const FwdPlan &p, int32_t hq, int32_t d) {
+  FwdLayout L;
+  L.split_tiles = (size_t)n * kItemWords * sizeof(int32_t);
+  const size_t np = (size_t)p.n_parts * hq;
+  L.part_lse = align_up(L.split_tiles + p.split_tiles.size() * sizeof(int32_t));
+  L.part_o = align_up(L.part_lse + np * kFwdBM * sizeof(float));
+  L.bytes = p.n_parts ? align_up(L.part_o + np * kFwdBM * (size_t)d * sizeof(float)) : align_up(L.split_tiles);
+  return L;
+}
 
 // ----------------------------------------------------------- backward table
 struct BwdPlan {
@@ -263,7 +336,10 @@ extern "C" int segattn_fwd_workspace(const segattn_shape *shape, const segattn_i
   if (!bytes) return fail(SEGATTN_E_INVALID, "%s: bytes is NULL", fn);
   if (int rc = check_shape(shape, fn)) return rc;
   if (int rc = check_items(shape, items, n_items, fn)) return rc;
-  *bytes = fwd_ws_bytes(n_items);
+  // enough for the call with or without SEGATTN_SPLIT_KEYS
+  FwdPlan plan;
+  build_fwd_plan(items, n_items, shape->hq, true, plan);
+  *bytes = fwd_layout(n_items, plan, shape->hq, shape->d).bytes;
   return SEGATTN_OK;
 }
 
@@ -279,29 +355,40 @@ extern "C" int segattn_fwd(const segattn_shape *shape, const void *q, const void
   if (int rc = check_ptr(o, fn, "o")) return rc;
   if (int rc = check_ptr(lse, fn, "lse")) return rc;
   if (o_dtype != SEGATTN_BF16 && o_dtype != SEGATTN_F32) return fail(SEGATTN_E_INVALID, "%s: o_dtype %d unknown", fn, o_dtype);
-  if (flags & ~SEGATTN_MERGE_INTO) return fail(SEGATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if (flags & ~(SEGATTN_MERGE_INTO | SEGATTN_SPLIT_KEYS)) return fail(SEGATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
   if ((flags & SEGATTN_MERGE_INTO) && o_dtype != SEGATTN_F32)
     return fail(SEGATTN_E_INVALID, "%s: SEGATTN_MERGE_INTO needs an fp32 output", fn);
   if (int rc = check_items(shape, items, n_items, fn)) return rc;
   if (int rc = check_disjoint_q(items, n_items, fn)) return rc;
-  const size_t need = fwd_ws_bytes(n_items);
+  FwdPlan plan;
+  build_fwd_plan(items, n_items, shape->hq, (flags & SEGATTN_SPLIT_KEYS) != 0, plan);
+  const FwdLayout lay = fwd_layout(n_items, plan, shape->hq, shape->d);
+  const size_t need = lay.bytes;
   if (!workspace || ws_bytes < need)
     return fail(SEGATTN_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
   if (!aligned16(workspace)) return fail(SEGATTN_E_INVALID, "%s: workspace is not 16-byte aligned", fn);
 
-  FwdPlan plan;
-  build_fwd_plan(items, n_items, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t *table = static_cast<int32_t *>(workspace);
-  if (hipError_t e = launch_upload(table, plan.words.data(), (int64_t)plan.words.size(), s)) return device_error(e, fn);
+  char *ws = static_cast<char *>(workspace);
+  int32_t *table = reinterpret_cast<int32_t *>(ws);
+  const int32_t n_split = (int32_t)(plan.split_tiles.size() / kSplitTileWords);
+  // Small tables travel in the kernel arguments; larger ones (the item
+  // table, then the split-tile table) are uploaded into the workspace.
+  const bool inline_tables = n_items <= kInlineItems && n_split <= kInlineSplitTiles;
+  if (!inline_tables) {
+    std::vector<int32_t> words = plan.words;
+    words.insert(words.end(), plan.split_tiles.begin(), plan.split_tiles.end());
+    if (hipError_t e = launch_upload(table, words.data(), (int64_t)words.size(), s)) return device_error(e, fn);
+  }
 
-  FwdArgs a;
+  FwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.lse = lse;
-  a.items = table;
+  a.items = inline_tables ? nullptr : table;
+  if (inline_tables) std::copy(plan.words.begin(), plan.words.end(), a.inline_items);
   a.n_items = n_items;
   a.n_units = plan.n_units;
   a.tokens = shape->tokens;
@@ -309,8 +396,21 @@ extern "C" int segattn_fwd(const segattn_shape *shape, const void *q, const void
   a.hkv = shape->hkv;
   a.scale_log2 = shape->scale * 1.4426950408889634f;
   a.merge = (flags & SEGATTN_MERGE_INTO) ? 1 : 0;
+  a.part_lse = plan.n_parts ? reinterpret_cast<float *>(ws + lay.part_lse) : nullptr;
+  a.part_o = plan.n_parts ? reinterpret_cast<float *>(ws + lay.part_o) : nullptr;
+  SplitMergeArgs m{};
+  m.tiles = inline_tables ? nullptr : reinterpret_cast<const int32_t *>(ws + lay.split_tiles);
+  if (inline_tables) std::copy(plan.split_tiles.begin(), plan.split_tiles.end(), m.inline_tiles);
+  m.n_tiles = n_split;
+  m.hq = shape->hq;
+  m.tokens = shape->tokens;
+  m.part_lse = a.part_lse;
+  m.part_o = a.part_o;
+  m.o = o;
+  m.lse = lse;
+  m.merge = a.merge;
   if ((int64_t)a.n_units * a.hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
-  if (hipError_t e = launch_fwd(a, shape->d, shape->in_dtype, o_dtype, s)) return device_error(e, fn);
+  if (hipError_t e = launch_fwd(a, m, shape->d, shape->in_dtype, o_dtype, s)) return device_error(e, fn);
   return SEGATTN_OK;
 }
 

@@ -17,6 +17,7 @@
 // item, over the visible keys j (k_lo <= j < k_hi, j <= q),
 //   LSE_q = log sum_j exp(scale <Q_q, K_j>),   O_q = sum_j exp(scale <Q_q,K_j> - LSE_q) V_j,
 // optionally merged into an existing fp32 (O, LSE) with the log-sum-exp rule.
+#include <cstddef>
 #include <type_traits>
 
 #include "device_common.h"
@@ -42,8 +43,18 @@ struct FwdCfg {
 static_assert(kFwdBN == kTileRows && kFwdBM == kFwdWaves * kFwdWaveRows && kFwdWaveRows % 16 == 0,
               "forward tile shape");
 
+// Tables are read through the constant address space (scalar loads):
+// either a device table or one carried in the kernel arguments, whose
+// explicit part starts at the kernel argument segment pointer.
+typedef const __attribute__((address_space(4))) int32_t *ctab;
+template <typename Args>
+__device__ __forceinline__ ctab arg_table(const int32_t *dev, size_t inline_offset) {
+  if (dev) return (ctab)dev;
+  return (ctab)((const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr() + inline_offset);
+}
+
 // Index of the item whose unit range holds `rank` (unit_begin ascending).
-__device__ __forceinline__ int find_item(const int32_t *items, int n, int rank) {
+__device__ __forceinline__ int find_item(ctab items, int n, int rank) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -80,9 +91,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
 
   int rank, h;
   map_xcd(blockIdx.x, a.hq, a.n_units, rank, h);
-  const int32_t *it = a.items + find_item(a.items, a.n_items, rank) * kItemWords;
+  const ctab items = arg_table<FwdArgs>(a.items, offsetof(FwdArgs, inline_items));
+  const ctab it = items + find_item(items, a.n_items, rank) * kItemWords;
   const int seq_off = it[0], q_lo = it[1], q_hi = it[2], k_lo = it[3], k_hi = it[4];
-  const int tile = rank - it[5];
+  // Work unit = (query tile, key piece): P pieces per query tile (P = 1
+  // unless the launch splits key walks), part0 = the item's first partial.
+  const int P = it[6], part0 = it[7];
+  const int local = rank - it[5];
+  const int tile = local / P, piece = local - tile * P;
   const int r1 = q_hi - tile * C::BM;             // heaviest (last) rows first
   const int r0 = max(q_lo, r1 - C::BM);
   const int hq = a.hq, hkv = a.hkv;
@@ -121,9 +137,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) coff[mt] = col_read_off<D>(mt, l16, lg);
 
-  const int kb = k_lo;
+  // This piece's 64-key tiles: its share [t0, t1) of the query tile's tiles.
   const int ke = min(k_hi, r1);
-  const int ntiles = ke > kb ? (ke - kb + C::BN - 1) / C::BN : 0;
+  const int nall = ke > k_lo ? (ke - k_lo + C::BN - 1) / C::BN : 0;
+  const int t0 = piece * nall / P, t1 = (piece + 1) * nall / P;
+  const int kb = k_lo + t0 * C::BN;
+  const int ntiles = t1 - t0;
 
   float m_run[C::NQ];
   // Row sums of P on the matrix unit: an extra O^T block whose A operand is
@@ -149,8 +168,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   // tile copies in flight included) before their first use in every step.
   wait_vm<0>();
   using Loader = TileLoader<D, InT, C::W>;
-  Loader lkv;
+  // bf16 input: direct global -> LDS copies, NS - 1 tiles ahead.  fp32 input
+  // (rounded to bf16 on the way): the tile NS - 1 ahead is fetched into
+  // registers in one step and rounded into its slot in the next, so no step
+  // waits for a global load of its own.
+  constexpr bool kViaRegs = std::is_same<InT, float>::value;
+  Loader lkv, lv;  // lv: the fp32 path's V registers
   lkv.init(wave, lane, kvstride);
+  lv.init(wave, lane, kvstride);
   auto stage = [&](int kvs, int slot) __attribute__((always_inline)) {
     __bf16 *Ks = lds + slot * C::BUF;
     const uint32_t ka = lds0 + slot * C::BUF * 2;  // its LDS byte address
@@ -158,23 +183,64 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
     lkv.template stage<kRowTile>(Ks, ka, kg + off, ke - kvs);
     lkv.template stage<kColTile>(Ks + C::TSZ, ka + C::TSZ * 2, vg + off, ke - kvs);
   };
+  auto fetch = [&](int kvs) __attribute__((always_inline)) {
+    if constexpr (kViaRegs) {
+      const int64_t off = ((int64_t)(seq_off + kvs) * hkv + g) * D;
+      lkv.fetch(kg + off, ke - kvs);
+      lv.fetch(vg + off, ke - kvs);
+    }
+  };
+  auto commit = [&](int slot) __attribute__((always_inline)) {
+    if constexpr (kViaRegs) {
+      __bf16 *Ks = lds + slot * C::BUF;
+      lkv.template commit<kRowTile>(Ks);
+      lv.template commit<kColTile>(Ks + C::TSZ);
+    }
+  };
 
   const float c2 = a.scale_log2;
-  int issued = 0, j = 0;
+  int issued = 0, j = 0;  // tiles staged (fp32: fetched) / steps done
+  bool pending = false;   // fp32: a fetched tile waits for its slot
+  if constexpr (kViaRegs) {
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+    for (int s = 0; s < NS - 2; ++s)
+      if (issued < ntiles) {
+        stage(kb + issued * C::BN, s);
+        ++issued;
+      }
     if (issued < ntiles) {
-      stage(kb + issued * C::BN, s);
+      fetch(kb + issued * C::BN);
       ++issued;
+      pending = true;
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (issued < ntiles) {
+        stage(kb + issued * C::BN, s);
+        ++issued;
+      }
+  }
 
   // One key tile.  The ring slot is a compile-time constant so every LDS
   // read is a precomputed lane offset plus an immediate.
   auto step = [&](auto slot) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(slot)::value;
-    wait_stages<2 * Loader::kInstr, NS>(issued - j - 1);
+    if constexpr (!kViaRegs) wait_stages<2 * Loader::kInstr, NS>(issued - j - 1);
     ring_barrier();  // tile `buf` visible; the slot staged next is free
-    if (issued < ntiles) {
+    if constexpr (kViaRegs) {
+      // tile j + NS - 2 (fetched last step) into the slot tile j - 2 used;
+      // the barriers of steps j + 1 .. j + NS - 2 publish it
+      if (pending) {
+        commit((buf + NS - 2) % NS);
+        pending = false;
+      }
+      if (issued < ntiles) {
+        fetch(kb + issued * C::BN);
+        ++issued;
+        pending = true;
+      }
+    } else if (issued < ntiles) {
       stage(kb + issued * C::BN, (buf + NS - 1) % NS);
       ++issued;
     }
@@ -317,15 +383,40 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
     while (ring_pass<0, NS>(step)) {
     }
 
-  // ---- epilogue: normalise, optional merge, write O rows and LSE.
-  OutT *__restrict__ og = static_cast<OutT *>(a.o);
+  // ---- epilogue: normalise; a key piece stores its partial; a whole
+  // query tile merges into (O, LSE) if asked and stores its rows.
+  float lse_row[C::NQ];
 #pragma unroll
   for (int nq = 0; nq < C::NQ; ++nq) {
     const float lt = lsum[nq][0];
+    lse_row[nq] = lt > 0.f ? (m_run[nq] + fast_log2(lt)) * kLn2 : kNegInf;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) o[nq][mt] *= inv;
+  }
+  if (P > 1) {
+    // A key piece of a split query tile: its normalised partial goes to
+    // partial (part0 + tile P + piece) of head h, rows local to the tile;
+    // split_merge_kernel, next on the stream, combines the pieces.
+    const int64_t pr0 = ((int64_t)(part0 + tile * P + piece) * hq + h) * C::BM;
+#pragma unroll
+    for (int nq = 0; nq < C::NQ; ++nq) {
+      const int qrow = rw0 + 16 * nq + l16;
+      if (has_rows && qrow < r1) {
+        const int64_t pr = pr0 + (qrow - r0);
+        if (lg == 0) a.part_lse[pr] = lse_row[nq];
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) *reinterpret_cast<f32x4 *>(a.part_o + pr * D + 16 * mt + 4 * lg) = o[nq][mt];
+      }
+    }
+    return;
+  }
+  OutT *__restrict__ og = static_cast<OutT *>(a.o);
+#pragma unroll
+  for (int nq = 0; nq < C::NQ; ++nq) {
     const int qrow = rw0 + 16 * nq + l16;
     const bool valid = has_rows && qrow < r1;
-    const float lse_new = lt > 0.f ? (m_run[nq] + fast_log2(lt)) * kLn2 : kNegInf;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_new = lse_row[nq];
     const int64_t grow = (int64_t)seq_off + (valid ? qrow : r0);
     float w_new = 1.f, w_old = 0.f, lse_out = lse_new;
     if (a.merge && valid) {
@@ -344,10 +435,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
     }
     if (valid) {
       OutT *op = og + (grow * hq + h) * D + 4 * lg;
-      const float sc = inv * w_new;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
-        f32x4 val = o[nq][mt] * sc;
+        f32x4 val = o[nq][mt] * w_new;
         if constexpr (sizeof(OutT) == 4) {
           if (a.merge) val += *reinterpret_cast<const f32x4 *>(op + 16 * mt) * w_old;
         }
@@ -358,24 +448,100 @@ __global__ __launch_bounds__(64 * kFwdWaves, kFwdWaveRows > 32 ? 1 : 2) void fwd
   }
 }
 
+// Combines the key pieces of split query tiles (SEGATTN_SPLIT_KEYS): for
+// each row, the log-sum-exp merge of its P partials in piece order (the
+// rule of segattn_merge applied left to right), then, as the forward's own
+// epilogue does, the optional merge into the (O, LSE) already held, and the
+// stores.  One thread per (row, 4 columns) of a split query tile and head,
+// D/4 workgroups per (tile, head): every load of a row is in flight at once
+// (the pieces are few and the merge is latency-bound).
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  constexpr int CPR = D / 4;  // 4-column chunks per row
+  constexpr int BPT = kFwdBM * CPR / 256;  // workgroups per (tile, head)
+  const int x = blockIdx.x, th = x / BPT, t = th / a.hq, h = th - t * a.hq;
+  const ctab st = arg_table<SplitMergeArgs>(a.tiles, offsetof(SplitMergeArgs, inline_tiles)) + t * kSplitTileWords;
+  const int seq_off = st[0], r0 = st[1], r1 = st[2], P = st[3], part = st[4];
+  const int w = (x - th * BPT) * 256 + threadIdx.x;
+  const int lr = w / CPR, c = w - lr * CPR;
+  if (lr >= r1 - r0) return;
+  const int64_t pstep = (int64_t)a.hq * kFwdBM;
+  const int64_t pr0 = ((int64_t)part * a.hq + h) * kFwdBM + lr;
+  float l[kFwdMaxPieces];
+  f32x4 ov[kFwdMaxPieces];
+#pragma unroll
+  for (int p = 0; p < kFwdMaxPieces; ++p) {
+    l[p] = p < P ? a.part_lse[pr0 + p * pstep] : kNegInf;
+    ov[p] = p < P ? *reinterpret_cast<const f32x4 *>(a.part_o + (pr0 + p * pstep) * D + 4 * c)
+                  : (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int p = 0; p < kFwdMaxPieces; ++p) m = fmaxf(m, l[p]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int p = 0; p < kFwdMaxPieces; ++p) {
+      if (p < P) {
+        const float wgt = fast_exp2((l[p] - m) * kLog2e);
+        den += wgt;
+        acc += wgt * ov[p];
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float lse_new = den > 0.f ? m + fast_log2(den) * kLn2 : kNegInf;
+  const int64_t grow = (int64_t)seq_off + r0 + lr;
+  float w_new = 1.f, w_old = 0.f, lse_out = lse_new;
+  if (a.merge) {
+    const float lo_ = a.lse[(int64_t)h * a.tokens + grow];
+    const float mm = fmaxf(lo_, lse_new);
+    if (mm == kNegInf) {
+      w_new = 0.f;
+      lse_out = kNegInf;
+    } else {
+      const float eo = fast_exp2((lo_ - mm) * kLog2e), en = fast_exp2((lse_new - mm) * kLog2e);
+      const float dd = eo + en;
+      w_old = eo / dd;
+      w_new = en / dd;
+      lse_out = mm + fast_log2(dd) * kLn2;
+    }
+  }
+  OutT *op = static_cast<OutT *>(a.o) + (grow * a.hq + h) * D + 4 * c;
+  f32x4 val = acc * (inv * w_new);
+  if constexpr (sizeof(OutT) == 4) {
+    if (a.merge) val += *reinterpret_cast<const f32x4 *>(op) * w_old;
+  }
+  store4<OutT>(op, val);
+  if (c == 0) a.lse[(int64_t)h * a.tokens + grow] = lse_out;
+}
+
 template <int D, typename InT, typename OutT>
-static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdArgs &a, const SplitMergeArgs &m, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_units * a.hq;
   hipLaunchKernelGGL((fwd_kernel<D, InT, OutT>), dim3((unsigned)grid), dim3(64 * FwdCfg<D>::W), 0, s, a);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (m.n_tiles > 0) {
+    constexpr int BPT = kFwdBM * (D / 4) / 256;
+    hipLaunchKernelGGL((split_merge_kernel<D, OutT>), dim3((unsigned)((int64_t)m.n_tiles * m.hq * BPT)), dim3(256), 0,
+                       s, m);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace dev
 
-hipError_t launch_fwd(const FwdArgs &a, int d, int in_dtype, int o_dtype, hipStream_t s) {
+hipError_t launch_fwd(const FwdArgs &a, const SplitMergeArgs &m, int d, int in_dtype, int o_dtype, hipStream_t s) {
   using namespace dev;
   const bool in_bf = in_dtype == 0, out_bf = o_dtype == 0;
   if (d == 128) {
-    if (in_bf) return out_bf ? launch_fwd_t<128, __bf16, __bf16>(a, s) : launch_fwd_t<128, __bf16, float>(a, s);
-    return out_bf ? launch_fwd_t<128, float, __bf16>(a, s) : launch_fwd_t<128, float, float>(a, s);
+    if (in_bf) return out_bf ? launch_fwd_t<128, __bf16, __bf16>(a, m, s) : launch_fwd_t<128, __bf16, float>(a, m, s);
+    return out_bf ? launch_fwd_t<128, float, __bf16>(a, m, s) : launch_fwd_t<128, float, float>(a, m, s);
   }
-  if (in_bf) return out_bf ? launch_fwd_t<64, __bf16, __bf16>(a, s) : launch_fwd_t<64, __bf16, float>(a, s);
-  return out_bf ? launch_fwd_t<64, float, __bf16>(a, s) : launch_fwd_t<64, float, float>(a, s);
+  if (in_bf) return out_bf ? launch_fwd_t<64, __bf16, __bf16>(a, m, s) : launch_fwd_t<64, __bf16, float>(a, m, s);
+  return out_bf ? launch_fwd_t<64, float, __bf16>(a, m, s) : launch_fwd_t<64, float, float>(a, m, s);
 }
 
 }  // namespace segattn

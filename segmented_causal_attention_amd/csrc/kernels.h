@@ -12,7 +12,8 @@ namespace segattn {
 // Device item table: one row of kItemWords int32 per work item.
 //   [0] seq_off  [1] q_lo  [2] q_hi  [3] k_lo  [4] k_hi   (sequence-local)
 //   [5] unit_begin: first work unit of this item in the launch's unit order
-//   [6] aux0  [7] aux1  (per-kernel meaning, see below)
+//   [6] aux0  [7] aux1  (per-kernel meaning: forward -- key pieces per query
+//   tile and the item's first partial result; see FwdArgs)
 constexpr int kItemWords = 8;
 
 // Forward tile shape: kFwdWaves wavefronts x kFwdWaveRows query rows per
@@ -42,17 +43,45 @@ constexpr int kBwdQBN = 64;
 constexpr int kBwdKvStages = 3;
 constexpr int kBwdQStages = 4;
 
+// Small launches carry their tables in the kernel arguments (no upload
+// launch): up to kInlineItems item rows, kInlineSplitTiles split tiles.
+constexpr int kInlineItems = 64;
+constexpr int kInlineSplitTiles = 64;
+
 struct FwdArgs {
   const void *q, *k, *v;
   void *o;
   float *lse;
-  const int32_t *items;  // device table, n_items rows
+  const int32_t *items;  // device table, n_items rows; NULL: inline_items
   int32_t n_items;
   int32_t n_units;       // query tiles over all items
   int64_t tokens;
   int32_t hq, hkv;
   float scale_log2;      // scale * log2(e)
   int32_t merge;         // 1: merge into the fp32 (O, LSE) already in o/lse
+  // Split query tiles (item word [6] = P > 1 key pieces): piece c of query
+  // tile t of an item whose first partial is f = word [7] writes partial
+  // (f + t P + c) of head h, index (f + t P + c) * hq + h, into part_lse
+  // [.][kFwdBM] and part_o [.][kFwdBM][d] (rows local to the tile).
+  float *part_lse, *part_o;
+  int32_t inline_items[kInlineItems * kItemWords];
+};
+
+// The pieces' combination, launched after the forward: one row of
+// kSplitTileWords int32 per split query tile:
+//   [0] seq_off  [1] r0  [2] r1 (its rows, sequence-local)  [3] P  [4] first partial
+constexpr int kSplitTileWords = 5;
+constexpr int kFwdMaxPieces = 8;  // key pieces per split query tile, at most
+struct SplitMergeArgs {
+  const int32_t *tiles;  // device table, n_tiles rows; NULL: inline_tiles
+  int32_t n_tiles;       // 0: nothing was split
+  int32_t hq;
+  int64_t tokens;
+  const float *part_lse, *part_o;
+  void *o;
+  float *lse;
+  int32_t merge;         // as FwdArgs::merge
+  int32_t inline_tiles[kInlineSplitTiles * kSplitTileWords];
 };
 
 // delta[h][t] = -D = -<dO[t,h,:], O[t,h,:]> for the query rows of the items
@@ -100,7 +129,7 @@ struct MergeArgs {
 
 // Launchers (return the hipError_t of the launch).  Template arguments are
 // resolved inside the .hip files from the runtime dtype codes.
-hipError_t launch_fwd(const FwdArgs &a, int d, int in_dtype, int o_dtype, hipStream_t s);
+hipError_t launch_fwd(const FwdArgs &a, const SplitMergeArgs &m, int d, int in_dtype, int o_dtype, hipStream_t s);
 hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);

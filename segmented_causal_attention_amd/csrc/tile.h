@@ -219,24 +219,38 @@ struct TileLoader<D, float, W> {
   static constexpr int kInstr = 0;  // nothing left in flight after stage()
   int64_t stride_;
   int tid_;
+  f32x4 raw_[N][2];  // a fetched tile, not yet rounded and written to LDS
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
     stride_ = stride;
     tid_ = wave * 64 + lane;
   }
-  template <int KIND>
-  __device__ __forceinline__ void stage(__bf16 *tile, uint32_t, const float *src, int nvalid) const {
-    u32x4 r[N];
+  // Issues the loads of one tile into registers (rows >= nvalid read as
+  // zeros); the compiler waits for them where commit() uses them.
+  __device__ __forceinline__ void fetch(const float *src, int nvalid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ch = tid_ + 64 * W * i, row = ch / CPR, c = ch % CPR;
-      r[i] = (row < kTileRows && row < nvalid) ? load8<float>(src + row * stride_ + 8 * c) : (u32x4){0, 0, 0, 0};
+      const bool ok = row < kTileRows && row < nvalid;
+      raw_[i][0] = ok ? *reinterpret_cast<const f32x4 *>(src + row * stride_ + 8 * c) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      raw_[i][1] = ok ? *reinterpret_cast<const f32x4 *>(src + row * stride_ + 8 * c + 4) : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
+  }
+  // Rounds the fetched tile to bf16 (nearest even) and writes it to LDS in
+  // layout KIND.
+  template <int KIND>
+  __device__ __forceinline__ void commit(__bf16 *tile) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ch = tid_ + 64 * W * i, row = ch / CPR, c = ch % CPR;
       if (row < kTileRows)
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(tile) + chunk_off<D, KIND>(row, c)) = r[i];
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(tile) + chunk_off<D, KIND>(row, c)) =
+            __builtin_bit_cast(u32x4, pack_bf16x8(raw_[i][0], raw_[i][1]));
     }
+  }
+  template <int KIND>
+  __device__ __forceinline__ void stage(__bf16 *tile, uint32_t, const float *src, int nvalid) {
+    fetch(src, nvalid);
+    commit<KIND>(tile);
   }
 };
 

@@ -44,20 +44,47 @@ hipError_t launch_upload(int32_t *dst, const int32_t *words, int64_t n, hipStrea
   return hipSuccess;
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int d, int in_dtype, int o_dtype, hipStream_t) {
+hipError_t launch_fwd(const FwdArgs &a, const SplitMergeArgs &m, int d, int in_dtype, int o_dtype, hipStream_t) {
   require(d == 64 || d == 128, "fwd d");
   require(in_dtype == 0 || in_dtype == 1, "fwd in_dtype");
   require(o_dtype == 0 || o_dtype == 1, "fwd o_dtype");
   require(a.n_items >= 1 && a.n_units >= 1, "fwd sizes");
+  const int32_t *items = a.items ? a.items : a.inline_items;
+  require(a.items || a.n_items <= kInlineItems, "inline item table size");
   // units: item i owns [unit_begin_i, unit_begin_{i+1}), ascending from 0
   int32_t prev = -1;
+  int64_t split_tiles = 0;
   for (int i = 0; i < a.n_items; ++i) {
-    const int32_t *w = a.items + i * kItemWords;
+    const int32_t *w = items + i * kItemWords;
     require(w[5] > prev && w[5] < a.n_units, "fwd unit order");
     require(w[2] > w[1] && w[4] > w[3] && w[4] <= w[2], "fwd item ranges");
+    require(w[6] >= 1 && w[6] <= 8, "fwd pieces");
     prev = w[5];
+    if (w[6] > 1) {
+      // touch every partial the pieces write, so that AddressSanitizer
+      // checks them against the (host) workspace
+      require(a.part_lse && a.part_o, "fwd split buffers");
+      const int tiles = (w[2] - w[1] + kFwdBM - 1) / kFwdBM;
+      for (int t = 0; t < tiles; ++t)
+        for (int c = 0; c < w[6]; ++c)
+          for (int h = 0; h < a.hq; ++h) {
+            const int64_t pr = ((int64_t)(w[7] + t * w[6] + c) * a.hq + h) * kFwdBM;
+            a.part_lse[pr] = a.part_lse[pr + kFwdBM - 1] = 0.f;
+            a.part_o[pr * d] = a.part_o[(pr + kFwdBM) * d - 1] = 0.f;
+          }
+      split_tiles += tiles;
+    }
   }
-  require(a.items[5] == 0, "fwd first unit");
+  require(items[5] == 0, "fwd first unit");
+  // the merge's tile table: rows within their item, partials within range
+  require(m.n_tiles == split_tiles, "split tile count");
+  for (int t = 0; t < m.n_tiles; ++t) {
+    const int32_t *st = (m.tiles ? m.tiles : m.inline_tiles) + t * kSplitTileWords;
+    require(st[2] > st[1] && st[2] - st[1] <= kFwdBM && st[3] > 1, "split tile rows");
+    const int64_t last = ((int64_t)(st[4] + st[3] - 1) * m.hq + m.hq - 1) * kFwdBM + (st[2] - st[1]) - 1;
+    volatile float x = m.part_lse[last];
+    (void)x;
+  }
   ++g_launches;
   return hipSuccess;
 }

@@ -182,7 +182,7 @@ def _fwd(shape, rows, o_dtype=0, flags=0, ws=FAKE, ws_bytes=1 << 20, ptrs=None):
     (_shape(), [[-1, 0, 8, 0, 8]], {}, _lib.SEGATTN_E_RANGE),
     (_shape(), [[0, 0, 8, 0, 8], [0, 4, 12, 0, 8]], {}, _lib.SEGATTN_E_INVALID),  # overlapping rows
     (_shape(), [[0, 0, 8, 0, 8]], {"flags": 1, "o_dtype": 0}, _lib.SEGATTN_E_INVALID),  # merge needs fp32
-    (_shape(), [[0, 0, 8, 0, 8]], {"flags": 8}, _lib.SEGATTN_E_INVALID),
+    (_shape(), [[0, 0, 8, 0, 8]], {"flags": 16}, _lib.SEGATTN_E_INVALID),  # unknown flag
     (_shape(), [[0, 0, 8, 0, 8]], {"o_dtype": 7}, _lib.SEGATTN_E_INVALID),
     (_shape(), [[0, 0, 8, 0, 8]], {"ws_bytes": 4}, _lib.SEGATTN_E_WORKSPACE),
     (_shape(), [[0, 0, 8, 0, 8]], {"ws": None}, _lib.SEGATTN_E_WORKSPACE),

@@ -150,18 +150,21 @@ def test_merge_kernel_other_head_dims(rows, h, d):
     assert_close_o(LB, rl, "LSE in place")
 
 
-def test_indexing_probe_zero_keys():
+@pytest.mark.parametrize("split", [False, True])
+def test_indexing_probe_zero_keys(split):
     """K = 0 makes every visible score exactly 0, so LSE_q = ln(count_q) where
     count_q is the number of keys the item lets row q see; exp(LSE) rounds
-    back to that integer, pinning every segment and block boundary."""
+    back to that integer, pinning every segment and block boundary (and,
+    with key pieces, every piece boundary: the merged LSE is ln of the sum of
+    the pieces' counts)."""
     S, N, block = 777, 3, 100
     hq = hkv = 2
-    say(f"case probe S={S} N={N} block={block}")
+    say(f"case probe S={S} N={N} block={block} split={split}")
     q, k, v = _inputs(15, S, hq, hkv, 128)
     k.zero_()
     b = sa.segattn_partition(S, N)
     for it in sa.segattn_ring_items(b, block):
-        o, lse = sa.segattn_fwd(q, k, v, it[None, :], o_dtype=torch.float32)
+        o, lse = sa.segattn_fwd(q, k, v, it[None, :], o_dtype=torch.float32, split_keys=split)
         torch.cuda.synchronize()
         _, ql, qh, kl, kh = it.tolist()
         rows = np.arange(ql, qh)
@@ -190,3 +193,48 @@ def test_c2_full_size_sampled_rows():
                                        rows, 1 / math.sqrt(d))
         assert_close_o(o[rows, h], ro, f"O h={h}")
         assert_close_o(lse[h, rows], rl, f"LSE h={h}")
+
+
+@pytest.mark.parametrize("case", ["c1_fp32", "gqa_bf16", "ring_merge", "short_pieces"])
+def test_split_keys(case):
+    """SEGATTN_SPLIT_KEYS: query tiles of a small launch cut into key pieces
+    on separate workgroups, combined by the last piece with the log-sum-exp
+    merge.  Against the oracle at the usual bars, close to the unsplit call,
+    and bit-identical on a second run."""
+    if case == "c1_fp32":
+        w = WORKLOADS["seg1k_fp32"]
+        T, hq, hkv, d, dt, seed = w["S"], 1, 1, w["d"], "fp32", w["seed"]
+        items, odt = segments(sa.segattn_partition(T, w["N"])), torch.float32
+    elif case == "gqa_bf16":
+        T, hq, hkv, d, dt, seed = 1500, 4, 2, 128, "bf16", 41
+        items, odt = segments(sa.segattn_partition(T, 3)), torch.bfloat16
+    elif case == "ring_merge":
+        T, hq, hkv, d, dt, seed = 1500, 3, 3, 64, "bf16", 42
+        items, odt = sa.segattn_ring_items(sa.segattn_partition(T, 5), 256), torch.float32
+    else:  # first query tiles see fewer key tiles than the item's piece count: empty pieces
+        T, hq, hkv, d, dt, seed = 600, 1, 1, 128, "bf16", 43
+        items, odt = np.array([[0, 0, 600, 0, 600]], np.int64), torch.float32
+    scale = 1 / math.sqrt(d)
+    say(f"case split keys {case} T={T} hq={hq} hkv={hkv} d={d} {dt}")
+    q, k, v = _inputs(seed, T, hq, hkv, d, dtype=dt)
+
+    def run(split):
+        if case == "ring_merge":
+            o = torch.zeros((T, hq, d), dtype=torch.float32, device=DEV)
+            lse = torch.full((hq, T), -math.inf, dtype=torch.float32, device=DEV)
+            for s_, st in enumerate(ring_steps(items)):
+                sa.segattn_fwd(q, k, v, st, o=o, lse=lse, merge_into=s_ > 0, split_keys=split)
+            return o, lse
+        return sa.segattn_fwd(q, k, v, items, o_dtype=odt, split_keys=split)
+
+    o1, l1 = run(True)
+    o2, l2 = run(True)
+    o0, l0 = run(False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "split result differs between runs"
+    ro, rl = oracle.attention_fwd(_bf16_host(q), _bf16_host(k), _bf16_host(v), None, scale)
+    assert_close_o(o1.float(), ro, "O split")
+    assert_close_o(l1, rl, "LSE split")
+    ma, rel = errors(o1.float(), host64(o0.float()))
+    say(f"  split vs unsplit O: max_abs={ma:.2e} rel_l2={rel:.2e}")
+    assert rel <= 5e-3
