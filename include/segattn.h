@@ -175,13 +175,14 @@ int segattn_fwd_workspace(const segattn_shape *shape, const segattn_item *items,
  * SEGATTN_F32); lse: device float [hq][tokens].  Only the items' rows are
  * written.  flags: 0, or SEGATTN_MERGE_INTO (o must be F32): the new partial
  * is merged into the (O, LSE) already held in o/lse with the log-sum-exp
- * rule of segattn_merge.  SEGATTN_SPLIT_KEYS (for latency): when the
- * launch has fewer than 256 (query tile, head) work units, the keys of each
- * long query tile are cut into up to 8 pieces of at least 2 64-key tiles,
- * computed by separate workgroups, and a second kernel on the stream
- * combines them with the same log-sum-exp merge, in piece order (the
+ * rule of segattn_merge.  SEGATTN_SPLIT_KEYS (for launches too small to
+ * fill the GPU: fewer than 1024 (query tile, head) work units): the keys of
+ * each query tile may be cut into up to 8 pieces of at least 2 64-key
+ * tiles, computed by separate workgroups, and a second kernel on the
+ * stream combines them with the same log-sum-exp merge, in piece order (the
  * segmented-plus-merged evaluation of InfiniPipe section II-A within one
- * call).  Results are deterministic but rounded differently from the
+ * call).  The piece count is the one whose longest-first schedule on the
+ * GPU finishes first (at most 512 MiB of partials).  Results are deterministic but rounded differently from the
  * unsplit walk; without the flag a row's result does not depend on which
  * other items share the call.  workspace: device, >= segattn_fwd_workspace
  * bytes, which covers the call with or without the flag.  stream:

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libsegattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # HIP translation units (kernels, and the host layer that launches them)
-HIP_SOURCES = ["fwd.hip", "bwd.hip", "misc.hip", "api.cpp"]
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "bwd_dqfirst.hip", "misc.hip", "api.cpp"]
 # plain C++ (no HIP headers): the integer planner
 CPP_SOURCES = ["planner.cpp", "chunking.cpp"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "kernels.h"
@@ -91,20 +93,31 @@ int device_error(hipError_t e, const char *fn) {
 // each item's tiles run from its last rows to its first, so the whole unit
 // order is heaviest-first for a single sequence.
 //
-// Key pieces (SEGATTN_SPLIT_KEYS, and only for a launch of fewer than
-// kSplitGrid workgroups): the key tiles of each query tile of an item are
-// cut into P contiguous pieces, one workgroup each, whose partials (O, LSE)
-// a second kernel on the stream combines with the log-sum-exp merge.  P is
-// chosen per item so that a piece keeps at least kMinPieceTiles key tiles,
-// at most kMaxPieces pieces, and the whole launch at most kSplitMaxGrid
-// workgroups.  (Combining them inside the forward -- the last piece to
-// finish, found with an atomic ticket -- needed device-scope fences, which
-// write back and invalidate L2 across the XCDs: 6-12 us per launch, more
-// than the split saved.)
-constexpr int64_t kSplitGrid = 256;
-constexpr int64_t kSplitMaxGrid = 512;
+// Key pieces (SEGATTN_SPLIT_KEYS): the key tiles of each query tile of an
+// item are cut into P contiguous pieces, one workgroup each, whose partials
+// (O, LSE) a second kernel on the stream combines with the log-sum-exp
+// merge.  (Combining them inside the forward -- the last piece to finish,
+// found with an atomic ticket -- needed device-scope fences, which write
+// back and invalidate L2 across the XCDs: 6-12 us per launch, more than the
+// split saved.)
+//
+// P is chosen per launch from a longest-first schedule of its work units on
+// the GPU (kSlots workgroups at a time: one forward workgroup per CU), in
+// 64-key tile steps: a workgroup costs its key tiles plus kUnitOverhead,
+// and a split launch adds kMergeOverhead for the merge kernel (from the
+// small-launch kernel trace: about 4 us per workgroup, 0.8 us per key tile,
+// 2 us for the merge).  Candidates are P = 1, 2, 3, 4, 6, 8, capped per item
+// so that a piece keeps at least kMinPieceTiles key tiles, and limited to
+// kSplitMaxPartialBytes of partials; the least makespan wins (ties to fewer
+// pieces).  Launches of kSplitGrid or more units are never split: they fill
+// the GPU many times over.
+constexpr int64_t kSlots = 256;
+constexpr int64_t kSplitGrid = 4 * kSlots;
 constexpr int64_t kMinPieceTiles = 2;
 constexpr int64_t kMaxPieces = kFwdMaxPieces;
+constexpr int64_t kUnitOverhead = 5;
+constexpr int64_t kMergeOverhead = 3;
+constexpr int64_t kSplitMaxPartialBytes = int64_t(512) << 20;
 
 struct FwdPlan {
   std::vector<int32_t> words;
@@ -117,31 +130,65 @@ int64_t fwd_tiles(const segattn_item &it) { return (it.q_hi - it.q_lo + kFwdBM -
 int64_t fwd_key_tiles(const segattn_item &it) {
   return (std::min(it.k_hi, it.q_hi) - it.k_lo + kFwdBN - 1) / kFwdBN;
 }
-
-// Pieces per item (all 1 unless a split applies).
-std::vector<int64_t> fwd_pieces(const segattn_item *items, int32_t n, int32_t hq, bool split) {
-  std::vector<int64_t> P(n, 1);
-  int64_t grid = 0;
-  for (int32_t i = 0; i < n; ++i) grid += fwd_tiles(items[i]) * hq;
-  if (!split || grid >= kSplitGrid) return P;
-  for (int32_t i = 0; i < n; ++i) P[i] = std::max<int64_t>(1, std::min(kMaxPieces, fwd_key_tiles(items[i]) / kMinPieceTiles));
-  auto total = [&] {
-    int64_t g = 0;
-    for (int32_t i = 0; i < n; ++i) g += fwd_tiles(items[i]) * P[i] * hq;
-    return g;
-  };
-  while (total() > kSplitMaxGrid) {  // take pieces from the item with the most
-    int32_t b = 0;
-    for (int32_t i = 1; i < n; ++i)
-      if (P[i] > P[b]) b = i;
-    if (P[b] == 1) break;
-    --P[b];
-  }
-  return P;
+// Key tiles of query tile t of an item (t = 0: its last rows).
+int64_t fwd_unit_key_tiles(const segattn_item &it, int64_t t) {
+  const int64_t ke = std::min(it.k_hi, it.q_hi - t * kFwdBM);
+  return ke > it.k_lo ? (ke - it.k_lo + kFwdBN - 1) / kFwdBN : 0;
 }
 
-void build_fwd_plan(const segattn_item *items, int32_t n, int32_t hq, bool split, FwdPlan &p) {
-  const std::vector<int64_t> P = fwd_pieces(items, n, hq, split);
+// Longest-first list schedule of `costs` on kSlots workgroup slots.
+int64_t lpt_makespan(std::vector<int64_t> costs) {
+  std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> load;
+  for (int64_t i = 0; i < kSlots; ++i) load.push(0);
+  int64_t span = 0;
+  for (int64_t c : costs) {
+    const int64_t l = load.top() + c;
+    load.pop();
+    load.push(l);
+    span = std::max(span, l);
+  }
+  return span;
+}
+
+// Pieces per item (all 1 unless a split applies).
+std::vector<int64_t> fwd_pieces(const segattn_item *items, int32_t n, int32_t hq, int32_t d, bool split) {
+  std::vector<int64_t> best(n, 1);
+  int64_t grid = 0;
+  for (int32_t i = 0; i < n; ++i) grid += fwd_tiles(items[i]) * hq;
+  if (!split || grid >= kSplitGrid) return best;
+  auto makespan = [&](const std::vector<int64_t> &P, int64_t *parts) {
+    std::vector<int64_t> costs;
+    *parts = 0;
+    for (int32_t i = 0; i < n; ++i)
+      for (int64_t t = 0; t < fwd_tiles(items[i]); ++t) {
+        const int64_t c = fwd_unit_key_tiles(items[i], t);
+        for (int64_t p = 0; p < P[i]; ++p) {
+          const int64_t cp = (p + 1) * c / P[i] - p * c / P[i] + kUnitOverhead;
+          for (int32_t h = 0; h < hq; ++h) costs.push_back(cp);
+        }
+        if (P[i] > 1) *parts += P[i];
+      }
+    return lpt_makespan(costs) + (*parts ? kMergeOverhead : 0);
+  };
+  int64_t parts = 0;
+  int64_t best_span = makespan(best, &parts);
+  for (int64_t pc : {2, 3, 4, 6, 8}) {
+    if (pc > kMaxPieces) break;
+    std::vector<int64_t> P(n);
+    for (int32_t i = 0; i < n; ++i) P[i] = std::max<int64_t>(1, std::min(pc, fwd_key_tiles(items[i]) / kMinPieceTiles));
+    const int64_t span = makespan(P, &parts);
+    if ((int64_t)hq * parts * kFwdBM * (d + 1) * 4 > kSplitMaxPartialBytes) continue;
+    if (span < best_span) {
+      best_span = span;
+      best = P;
+    }
+  }
+  return best;
+}
+
+void build_fwd_plan(const segattn_item *items, int32_t n, int32_t hq, int32_t d, bool split, FwdPlan &p) {
+  const std::vector<int64_t> P = fwd_pieces(items, n, hq, d, split);
   std::vector<int32_t> order(n);
   for (int32_t i = 0; i < n; ++i) order[i] = i;
   auto cost = [&](int32_t i) { return (fwd_key_tiles(items[i]) + P[i] - 1) / P[i]; };
@@ -194,6 +241,9 @@ FwdLayout fwd_layout(int32_t n, const FwdPlan &p, int32_t hq, int32_t d) {
 struct BwdPlan {
   std::vector<int32_t> items, kvg, qg;
   int32_t n_kv_units = 0, n_q_units = 0;
+  // longest walk of each role in tile steps: a dQ workgroup's 64-key tiles,
+  // a dK/dV workgroup's 64-row tiles per query head of its group
+  int64_t kv_walk = 0, q_walk = 0;
 };
 
 int build_bwd_plan(const segattn_item *items, int32_t n, BwdPlan &p, const char *fn) {
@@ -280,6 +330,18 @@ int build_bwd_plan(const segattn_item *items, int32_t n, BwdPlan &p, const char 
     u += (g.ke - g.kb + kBwdKvBN - 1) / kBwdKvBN;
   }
   p.n_kv_units = (int32_t)u;
+  // a dK/dV workgroup walks, per query head of its group, the 64-row tiles
+  // of every item that sees its keys; the first key tile of a group sees
+  // the most
+  for (auto &g : kgs) {
+    int64_t walk = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const segattn_item &it = items[i];
+      if (it.seq_off == g.seq_off && it.k_lo < g.kb + kBwdKvBN && it.k_hi > g.kb && it.q_hi > g.kb)
+        walk += (it.q_hi - std::max(it.q_lo, g.kb) + kBwdKvBM - 1) / kBwdKvBM;
+    }
+    p.kv_walk = std::max(p.kv_walk, walk);
+  }
   p.qg.clear();
   u = 0;
   for (auto &q : qgs) {
@@ -287,6 +349,7 @@ int build_bwd_plan(const segattn_item *items, int32_t n, BwdPlan &p, const char 
     u += (q.hi - q.lo + kBwdQBM - 1) / kBwdQBM;
   }
   p.n_q_units = (int32_t)u;
+  for (auto &q : qgs) p.q_walk = std::max(p.q_walk, (q.cost + kBwdQBN - 1) / kBwdQBN);
   return SEGATTN_OK;
 }
 
@@ -338,7 +401,7 @@ extern "C" int segattn_fwd_workspace(const segattn_shape *shape, const segattn_i
   if (int rc = check_items(shape, items, n_items, fn)) return rc;
   // enough for the call with or without SEGATTN_SPLIT_KEYS
   FwdPlan plan;
-  build_fwd_plan(items, n_items, shape->hq, true, plan);
+  build_fwd_plan(items, n_items, shape->hq, shape->d, true, plan);
   *bytes = fwd_layout(n_items, plan, shape->hq, shape->d).bytes;
   return SEGATTN_OK;
 }
@@ -361,7 +424,7 @@ extern "C" int segattn_fwd(const segattn_shape *shape, const void *q, const void
   if (int rc = check_items(shape, items, n_items, fn)) return rc;
   if (int rc = check_disjoint_q(items, n_items, fn)) return rc;
   FwdPlan plan;
-  build_fwd_plan(items, n_items, shape->hq, (flags & SEGATTN_SPLIT_KEYS) != 0, plan);
+  build_fwd_plan(items, n_items, shape->hq, shape->d, (flags & SEGATTN_SPLIT_KEYS) != 0, plan);
   const FwdLayout lay = fwd_layout(n_items, plan, shape->hq, shape->d);
   const size_t need = lay.bytes;
   if (!workspace || ws_bytes < need)
@@ -496,7 +559,8 @@ int bwd_check(const char *fn, const segattn_shape *shape, const void *q, const v
   if (int rc = build_bwd_plan(items, n_items, plan, fn)) return rc;
   const int64_t kv_blocks = (int64_t)plan.n_kv_units * shape->hkv;
   const int64_t kv_pad = (kv_blocks + 7) / 8 * 8;
-  if (kv_pad + (int64_t)plan.n_q_units * shape->hq > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
+  const int64_t q_blocks = (int64_t)plan.n_q_units * shape->hq;
+  if (kv_pad + q_blocks + 8 > 0x7fffffffLL) return fail(SEGATTN_E_RANGE, "%s: grid too large", fn);
   return SEGATTN_OK;
 }
 
@@ -508,6 +572,8 @@ int bwd_launch(const char *fn, const segattn_shape *shape, const void *q, const 
                hipStream_t s) {
   const int64_t kv_blocks = (int64_t)plan.n_kv_units * shape->hkv;
   const int64_t kv_pad = (kv_blocks + 7) / 8 * 8;
+  const int64_t q_blocks = (int64_t)plan.n_q_units * shape->hq;
+  const int64_t q_pad = (q_blocks + 7) / 8 * 8;
   float *delta = static_cast<float *>(workspace);
   BwdTables t;
   if (hipError_t e = upload_bwd_tables(shape, plan, workspace, s, t)) return device_error(e, fn);
@@ -535,6 +601,9 @@ int bwd_launch(const char *fn, const segattn_shape *shape, const void *q, const 
   a.n_q_units = plan.n_q_units;
   a.kv_blocks = (int32_t)kv_blocks;
   a.kv_pad = (int32_t)kv_pad;
+  a.q_blocks = (int32_t)q_blocks;
+  a.q_pad = (int32_t)q_pad;
+  a.dq_first = plan.q_walk > plan.kv_walk * (shape->hq / shape->hkv) ? 1 : 0;
   a.tokens = shape->tokens;
   a.hq = shape->hq;
   a.hkv = shape->hkv;

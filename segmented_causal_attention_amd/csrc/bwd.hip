@@ -827,26 +827,47 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a, int x, char *smem) {
   }
 }
 
-// One launch for both roles: workgroups [0, kv_blocks) are dK/dV tiles,
-// [kv_pad, kv_pad + q blocks) dQ tiles (kv_pad = kv_blocks rounded up to a
-// multiple of the 8 XCDs so that both parts keep the head -> XCD map; the
-// padding workgroups exit at once).  dQ workgroups start as the dK/dV ones
-// drain, filling the tail of the longer part.
-template <int D, typename InT, typename GT>
+// One launch for both roles.  Normally workgroups [0, kv_blocks) are dK/dV
+// tiles and [kv_pad, kv_pad + q_blocks) dQ tiles, so the dQ workgroups start
+// as the dK/dV ones drain; when the dQ role's longest walk is the longer
+// one (a call over a few late segments: few query tiles, each against every
+// earlier key), the dQ role goes first instead, so that its long walks start
+// at once and the short dK/dV tiles fill in around them.  The second range
+// starts at a multiple of the 8 XCDs so that both keep the head -> XCD map;
+// the padding workgroups exit at once.
+template <int D, typename InT, typename GT, bool DQ_FIRST>
 __global__ __launch_bounds__(64 * kBwdKvWaves) void bwd_kernel(BwdArgs a) {
   static_assert(kBwdKvWaves == kBwdQWaves, "both roles use the same workgroup size");
   __shared__ __attribute__((aligned(16))) char smem[BwdLds<D>::kBytes];
   const int x = blockIdx.x;
-  if (x < a.kv_blocks)
-    dkdv_body<D, InT, GT>(a, x, smem);
-  else if (x >= a.kv_pad)
-    dq_body<D, InT, GT>(a, x - a.kv_pad, smem);
+  if constexpr (DQ_FIRST) {
+    if (x < a.q_blocks)
+      dq_body<D, InT, GT>(a, x, smem);
+    else if (x >= a.q_pad)
+      dkdv_body<D, InT, GT>(a, x - a.q_pad, smem);
+  } else {
+    if (x < a.kv_blocks)
+      dkdv_body<D, InT, GT>(a, x, smem);
+    else if (x >= a.kv_pad)
+      dq_body<D, InT, GT>(a, x - a.kv_pad, smem);
+  }
 }
+
+// Each role order is compiled in its own translation unit (this file, and
+// bwd_dqfirst.hip, which includes it with SEGATTN_BWD_DQ_FIRST defined):
+// with both kernels in one module the compiler inlined the shared helpers
+// differently and the dK/dV-first kernel grew from 13 to 27 spilled scalar
+// registers (+0.8% time).
+#ifdef SEGATTN_BWD_DQ_FIRST
+constexpr bool kDqFirstTU = true;
+#else
+constexpr bool kDqFirstTU = false;
+#endif
 
 template <int D, typename InT, typename GT>
 static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.kv_pad + (int64_t)a.n_q_units * a.hq;
-  hipLaunchKernelGGL((bwd_kernel<D, InT, GT>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0, s, a);
+  const int64_t grid = kDqFirstTU ? (int64_t)a.q_pad + a.kv_blocks : (int64_t)a.kv_pad + a.q_blocks;
+  hipLaunchKernelGGL((bwd_kernel<D, InT, GT, kDqFirstTU>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -863,9 +884,16 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     return gb ? dev::FN<64, float, __bf16>(a, s) : dev::FN<64, float, float>(a, s);       \
   } while (0)
 
-hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
+#ifdef SEGATTN_BWD_DQ_FIRST
+hipError_t launch_bwd_dq_first(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
   SEGATTN_DISPATCH(launch_bwd_t, a, d, in_dtype, g_dtype, s);
 }
+#else
+hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s) {
+  if (a.dq_first) return launch_bwd_dq_first(a, d, in_dtype, g_dtype, s);
+  SEGATTN_DISPATCH(launch_bwd_t, a, d, in_dtype, g_dtype, s);
+}
+#endif
 
 #undef SEGATTN_DISPATCH
 

@@ -112,7 +112,11 @@ struct BwdArgs {
   int32_t n_items, n_kvg, n_qg;
   int32_t n_kv_units, n_q_units;
   int32_t kv_blocks;     // n_kv_units * hkv: dK/dV workgroups
-  int32_t kv_pad;        // kv_blocks rounded up to a multiple of 8: first dQ workgroup
+  int32_t kv_pad;        // kv_blocks rounded up to a multiple of 8
+  int32_t q_blocks;      // n_q_units * hq: dQ workgroups
+  int32_t q_pad;         // q_blocks rounded up to a multiple of 8
+  int32_t dq_first;      // 1: workgroups [0, q_blocks) are dQ, then from q_pad dK/dV;
+                         // 0: [0, kv_blocks) dK/dV, then from kv_pad dQ
   int64_t tokens;
   int32_t hq, hkv;
   float scale, scale_log2;
@@ -132,6 +136,8 @@ struct MergeArgs {
 hipError_t launch_fwd(const FwdArgs &a, const SplitMergeArgs &m, int d, int in_dtype, int o_dtype, hipStream_t s);
 hipError_t launch_bwd_pre(const PreArgs &a, int d, int o_dtype, int in_dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
+// launch_bwd's kernel for a.dq_first (bwd_dqfirst.hip)
+hipError_t launch_bwd_dq_first(const BwdArgs &a, int d, int in_dtype, int g_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 // Copies n int32 words from host memory into dst (device) through kernel
 // arguments: stream-ordered, graph-capturable, no pageable-memory copy.

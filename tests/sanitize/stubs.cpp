@@ -101,6 +101,8 @@ hipError_t launch_bwd_pre(const PreArgs &a, int d, int, int, hipStream_t) {
 hipError_t launch_bwd(const BwdArgs &a, int d, int, int, hipStream_t) {
   require(d == 64 || d == 128, "bwd d");
   require(a.kv_pad >= a.kv_blocks && a.kv_pad % 8 == 0 && a.kv_pad - a.kv_blocks < 8, "bwd kv_pad");
+  require(a.q_pad >= a.q_blocks && a.q_pad % 8 == 0 && a.q_pad - a.q_blocks < 8, "bwd q_pad");
+  require(a.q_blocks == a.n_q_units * a.hq && (a.dq_first == 0 || a.dq_first == 1), "bwd q blocks");
   require(a.kv_blocks == a.n_kv_units * a.hkv, "bwd kv blocks");
   int32_t prev = -1;
   for (int g = 0; g < a.n_kvg; ++g) {
