@@ -70,7 +70,7 @@ PEAK_HBM_GBS = 8000.0
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # The device code; counter readings taken on other sources are not reported.
-KERNEL_SOURCES = ("fwd.hip", "bwd.hip", "misc.hip", "tile.h", "device_common.h", "kernels.h")
+KERNEL_SOURCES = ("fwd.hip", "bwd.hip", "bwd_dqfirst.hip", "misc.hip", "tile.h", "device_common.h", "kernels.h")
 
 
 def kernel_sources_sha256():
