@@ -2,7 +2,9 @@
 against the float64 oracle: head dim 64 / 128, grouped-query ratios 1..8,
 FLOPs-balanced segments, variable-length packed batches, ring-order blocks
 merged into an fp32 accumulator, bf16 and fp32 inputs and outputs, scales
-other than 1/sqrt(d), the accumulate and preprocess-first backward flags.
+other than 1/sqrt(d), the accumulate and preprocess-first backward flags,
+and key pieces in the forward (SEGATTN_SPLIT_KEYS, drawn from a stream of
+its own so that the other draws of a seed do not change).
 
 Each case prints its seed and shape before touching the GPU; the parity bar
 is the one of the other GPU tests (O, LSE: max-abs <= 1e-2 and relative-L2
@@ -64,9 +66,11 @@ def _draw(seed):
 @pytest.mark.parametrize("seed", range(5000, 5048))
 def test_random_path(seed):
     c = _draw(seed)
+    split = bool(np.random.default_rng([seed, 1]).random() < 0.5)
     T, hq, hkv, d, scale = c["T"], c["hq"], c["hkv"], c["d"], c["scale"]
     say(f"case random seed={seed} kind={c['kind']} T={T} hq={hq} hkv={hkv} d={d} in={c['in_dtype']} "
-        f"o={c['o_dtype']} g={c['g_dtype']} acc={c['accumulate']} pre={c['preprocess']} items={len(c['items'])}")
+        f"o={c['o_dtype']} g={c['g_dtype']} acc={c['accumulate']} pre={c['preprocess']} split={split} "
+        f"items={len(c['items'])}")
     t = gen_tensors(seed, T, hq, hkv, d, dtype=c["in_dtype"], device=DEV)
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     items = c["items"]
@@ -76,9 +80,9 @@ def test_random_path(seed):
         o = torch.empty((T, hq, d), dtype=torch.float32, device=DEV)
         lse = torch.empty((hq, T), dtype=torch.float32, device=DEV)
         for s, st in enumerate(ring_steps(items)):
-            sa.segattn_fwd(q, k, v, st, scale=scale, o=o, lse=lse, merge_into=s > 0)
+            sa.segattn_fwd(q, k, v, st, scale=scale, o=o, lse=lse, merge_into=s > 0, split_keys=split)
     else:
-        o, lse = sa.segattn_fwd(q, k, v, items, scale=scale, o_dtype=c["o_dtype"])
+        o, lse = sa.segattn_fwd(q, k, v, items, scale=scale, o_dtype=c["o_dtype"], split_keys=split)
 
     # backward (items in reverse order)
     rev = np.ascontiguousarray(items[::-1])
