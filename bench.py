@@ -471,7 +471,10 @@ def c1_latency(torch, sa, synth, calls=500, warmup=50, per_graph=50, replays=10)
       graph_replay: the same call captured `per_graph` times into one HIP
         graph (torch.cuda.graph), replayed `replays` times: the GPU's time
         per call without the host path.  Every replay's outputs are checked
-        bit for bit against the eager call's."""
+        bit for bit against the eager call's;
+      split_prepared: eager calls of segattn_fwd_prepare's callable (the
+        binding's checks done once), outputs checked against the eager
+        call's."""
     w = synth.WORKLOADS["seg1k_fp32"]
     S, N, d = w["S"], w["N"], w["d"]
     t = synth.gen_tensors(w["seed"], S, w["hq"], w["hkv"], d, dtype="fp32", device="cuda")
@@ -530,6 +533,30 @@ def c1_latency(torch, sa, synth, calls=500, warmup=50, per_graph=50, replays=10)
         del g
         return float(np.median(times)), bool(same)
 
+    def prepared():
+        """Eager calls of one prepared call (arguments checked and converted
+        once): the host path without the binding's per-call work."""
+        call(True)
+        torch.cuda.synchronize()
+        ref_o, ref_l = o.clone(), lse.clone()
+        pc = sa.segattn_fwd_prepare(q, k, v, items, o=o, lse=lse, workspace=fws, split_keys=True)
+        for _ in range(warmup):
+            pc()
+        torch.cuda.synchronize()
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(calls):
+            pc()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        same = torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+        return e0.elapsed_time(e1) * 1e3 / calls, wall * 1e6 / calls, bool(same)
+
     res = {}
     for split in (False, True):
         gpu_us, host_us = eager(split)
@@ -538,6 +565,10 @@ def c1_latency(torch, sa, synth, calls=500, warmup=50, per_graph=50, replays=10)
             "gpu_us_per_call": round(gpu_us, 2), "host_us_per_call": round(host_us, 2),
             "graph_replay_us_per_call": round(g_us, 2), "graph_replays_bit_identical": same,
             "tflops_at_graph_time": round(flops / (g_us * 1e-6) / 1e12, 3)}
+    gpu_us, host_us, same = prepared()
+    res["split_prepared"] = {"gpu_us_per_call": round(gpu_us, 2), "host_us_per_call": round(host_us, 2),
+                             "bit_identical_to_split": same,
+                             "tflops_at_gpu_time": round(flops / (gpu_us * 1e-6) / 1e12, 3)}
     print(json.dumps({"latency": "fwd", "workload": w["name"], "segments": N, "bounds": b, "calls": calls,
                       "flops_per_call": flops, **res}), flush=True)
 

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     segattn_chunk_varlen,
     segattn_copy_rows,
     segattn_fwd,
+    segattn_fwd_prepare,
     segattn_fwd_workspace,
     segattn_merge,
     segattn_offload_plan,

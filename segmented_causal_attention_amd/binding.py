@@ -1,6 +1,7 @@
 """Python binding of libsegattn.so: argument marshalling only.
 
-Every function has the name of the C entry point it calls.  Device buffers are
+Every function has the name of the C entry point it calls
+(``segattn_fwd_prepare`` prepares a repeated ``segattn_fwd``).  Device buffers are
 torch tensors (torch provides device memory and the current HIP stream);
 item tables are host ``numpy.int64`` arrays of shape [n, 5] with columns
 (seq_off, q_lo, q_hi, k_lo, k_hi).  A nonzero status raises ``SegattnError``
@@ -176,11 +177,9 @@ def segattn_fwd_workspace(shape, items):
     return nb.value
 
 
-def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, merge_into=False,
-                split_keys=False, workspace=None, stream=None):
-    """Partial attention of `items` into (o, lse); returns (o, lse).
-    New outputs are allocated (o_dtype defaults to q's dtype; lse filled
-    with -inf) when not given.  split_keys sets SEGATTN_SPLIT_KEYS."""
+def _fwd_args(q, k, v, items, scale, o, o_dtype, lse, merge_into, split_keys, workspace, stream):
+    """Checked and converted arguments of one segattn_fwd call, the buffers
+    they point into (kept alive with them), and (o, lse)."""
     shape = make_shape(q, k, scale)
     _check_kv(q, k, v)
     arr, p, n = _items_arg(items)
@@ -193,10 +192,42 @@ def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, m
     ocode = _DTYPE_CODE[o.dtype]
     ws = _workspace(lambda: segattn_fwd_workspace(shape, arr), q.device, workspace)
     flags = (SEGATTN_MERGE_INTO if merge_into else 0) | (SEGATTN_SPLIT_KEYS if split_keys else 0)
-    check(lib().segattn_fwd(ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), p, n,
-                            _dev(o, "o"), ocode, _dev(lse, "lse", torch.float32), flags,
-                            _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(stream)))
+    args = (ctypes.byref(shape), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), p, n, _dev(o, "o"), ocode,
+            _dev(lse, "lse", torch.float32), flags, _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+            _stream(stream))
+    return args, (shape, q, k, v, arr, o, lse, ws), o, lse
+
+
+def segattn_fwd(q, k, v, items, *, scale=None, o=None, o_dtype=None, lse=None, merge_into=False,
+                split_keys=False, workspace=None, stream=None):
+    """Partial attention of `items` into (o, lse); returns (o, lse).
+    New outputs are allocated (o_dtype defaults to q's dtype; lse filled
+    with -inf) when not given.  split_keys sets SEGATTN_SPLIT_KEYS."""
+    args, _, o, lse = _fwd_args(q, k, v, items, scale, o, o_dtype, lse, merge_into, split_keys, workspace, stream)
+    check(lib().segattn_fwd(*args))
     return o, lse
+
+
+def segattn_fwd_prepare(q, k, v, items, *, o, lse, scale=None, merge_into=False, split_keys=False,
+                        workspace=None, stream=None):
+    """segattn_fwd with its arguments checked and converted once, for a call
+    repeated on the same buffers (a training or serving loop with fixed
+    shapes).  Returns a callable that issues the identical C call -- same
+    tensors, items, flags, workspace and stream (the current stream at
+    preparation when none is given) -- with no per-call Python work but the
+    foreign call itself.  The callable holds references to every tensor and
+    to the item table, so their memory stays valid; their contents may
+    change between calls, their storage must not be replaced."""
+    args, keep, _, _ = _fwd_args(q, k, v, items, scale, o, None, lse, merge_into, split_keys, workspace, stream)
+    fn = lib().segattn_fwd
+
+    def call():
+        st = fn(*args)
+        if st:
+            check(st)
+
+    call.buffers = keep
+    return call
 
 
 def segattn_merge(o_a, lse_a, o_b, lse_b, *, o_out=None, lse_out=None, rows=None, lse_stride=None,

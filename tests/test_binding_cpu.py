@@ -161,3 +161,15 @@ def test_merge_rejects(what):
         ob = ob.to(BF)
     with pytest.raises((ValueError, TypeError)):
         sa.segattn_merge(oa, la, ob, lb, **kw)
+
+
+# ------------------------------------------------------------------ prepared forward
+
+def test_fwd_prepare_checks_like_fwd():
+    q, k, v, _ = qkv()
+    o, lse = stats(F32)
+    reaches_device_check(lambda: sa.segattn_fwd_prepare(q, k, v, ITEMS, o=o, lse=lse))
+    with pytest.raises(ValueError, match="lse"):
+        sa.segattn_fwd_prepare(q, k, v, ITEMS, o=o, lse=torch.zeros(T, HQ, dtype=F32))
+    with pytest.raises(TypeError, match="v"):
+        sa.segattn_fwd_prepare(q, k, v.float(), ITEMS, o=o, lse=lse)
