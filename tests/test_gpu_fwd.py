@@ -238,3 +238,43 @@ def test_split_keys(case):
     ma, rel = errors(o1.float(), host64(o0.float()))
     say(f"  split vs unsplit O: max_abs={ma:.2e} rel_l2={rel:.2e}")
     assert rel <= 5e-3
+
+
+@pytest.mark.parametrize("split,merge", [(False, False), (True, False), (True, True)])
+def test_prepared_call_repeats_the_call(split, merge):
+    """segattn_fwd_prepare: the prepared callable issues the same C call as
+    segattn_fwd (bit-identical outputs), and each call reads the buffers'
+    contents at that time (new inputs written into the same tensors give the
+    new result)."""
+    T, hq, hkv, d = 1100, 2, 1, 64
+    say(f"case prepared call split={split} merge={merge} T={T} hq={hq} hkv={hkv} d={d}")
+    q, k, v = _inputs(61, T, hq, hkv, d)
+    items = segments(sa.segattn_partition(T, 4))
+    o = torch.zeros((T, hq, d), dtype=torch.float32, device=DEV)
+    lse = torch.full((hq, T), -math.inf, dtype=torch.float32, device=DEV)
+    if merge:  # a first partial to merge into, the same for both calls
+        sa.segattn_fwd(q, k, v, items, o=o, lse=lse)
+    o0, l0 = o.clone(), lse.clone()
+    call = sa.segattn_fwd_prepare(q, k, v, items, o=o, lse=lse, merge_into=merge, split_keys=split)
+    call()
+    ref_o, ref_l = o.clone(), lse.clone()
+    o.copy_(o0)
+    lse.copy_(l0)
+    sa.segattn_fwd(q, k, v, items, o=o, lse=lse, merge_into=merge, split_keys=split)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), "prepared call differs from segattn_fwd"
+    # new contents in the same buffers
+    q2, k2, v2 = _inputs(62, T, hq, hkv, d)
+    q.copy_(q2)
+    k.copy_(k2)
+    v.copy_(v2)
+    o.copy_(o0)
+    lse.copy_(l0)
+    call()
+    torch.cuda.synchronize()
+    if not merge:
+        ro, rl = oracle.attention_fwd(_bf16_host(q2), _bf16_host(k2), _bf16_host(v2), None, 1 / math.sqrt(d))
+        assert_close_o(o, ro, "O prepared, new inputs")
+        assert_close_o(lse, rl, "LSE prepared, new inputs")
+    else:
+        assert not torch.equal(o, ref_o), "prepared call did not read the new inputs"
