@@ -20,7 +20,10 @@ namespace dev {
 // before any store, so an in-place merge reads the old LSE in every lane
 // before a lane overwrites it.  A workgroup takes kMergeUnroll groups of
 // 256/(d/4) consecutive vectors with all their loads in flight at once; the
-// only 64-bit division is one per workgroup.
+// only 64-bit division is one per workgroup.  The O vectors are read and
+// written once, so their loads and stores carry the nontemporal hint (5.77
+// instead of 5.34 TB/s on 131072 x 32 x 128 partials); the LSE entries,
+// 4 bytes per vector spread over the heads' rows, keep the default policy.
 constexpr int kMergeUnroll = 4;
 
 __device__ __forceinline__ void merge_one(const MergeArgs &a, int64_t vec, int64_t li, int c, const f32x4 &oa,
@@ -34,7 +37,7 @@ __device__ __forceinline__ void merge_one(const MergeArgs &a, int64_t vec, int64
     out = oa * (wa * inv) + ob * (wb * inv);
     lse = m + fast_log2(den) * kLn2;
   }
-  *reinterpret_cast<f32x4 *>(a.o_out + vec * a.d + 4 * c) = out;
+  __builtin_nontemporal_store(out, reinterpret_cast<f32x4 *>(a.o_out + vec * a.d + 4 * c));
   if (c == 0) a.lse_out[li] = lse;
 }
 
@@ -58,8 +61,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int64_t vec = vbase + v;
     li[u] = (int64_t)(t % a.h) * a.lse_stride + r0 + t / a.h;
     if (vec < nvec) {
-      oa[u] = *reinterpret_cast<const f32x4 *>(a.o_a + vec * D + 4 * c);
-      ob[u] = *reinterpret_cast<const f32x4 *>(a.o_b + vec * D + 4 * c);
+      oa[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.o_a + vec * D + 4 * c));
+      ob[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.o_b + vec * D + 4 * c));
       la[u] = a.lse_a[li[u]];
       lb[u] = a.lse_b[li[u]];
     }
@@ -87,8 +90,8 @@ __global__ __launch_bounds__(256) void merge_kernel_any(MergeArgs a) {
     f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = oa;
     float la = kNegInf, lb = kNegInf;
     if (ok) {
-      oa = *reinterpret_cast<const f32x4 *>(a.o_a + vec * a.d + 4 * c);
-      ob = *reinterpret_cast<const f32x4 *>(a.o_b + vec * a.d + 4 * c);
+      oa = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.o_a + vec * a.d + 4 * c));
+      ob = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.o_b + vec * a.d + 4 * c));
       la = a.lse_a[li];
       lb = a.lse_b[li];
     }
