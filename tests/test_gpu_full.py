@@ -290,6 +290,15 @@ def test_million_forward_sampled_rows(million):
     _check_rows(t["q"], t["k"], t["v"], None, o, lse, None, 0, S, 0, 0, rows, scale, "1M", grads=False)
     rows2 = np.unique(np.concatenate([b[-2:-1], [S - 1], rng.integers(0, S, 30)]))
     _check_rows(t["q"], t["k"], t["v"], None, o, lse, None, 0, S, H - 1, H - 1, rows2, scale, "1M", grads=False)
+    # a few rows whose keys span the whole million, against the oracle's
+    # softmax over all their keys at once (one key block: no merge on the
+    # reference side, so the check does not lean on the merge it tests)
+    rows3 = np.array([S // 2, b[-2], S - 1], np.int64)
+    h = 7
+    ro, rl = oracle.attention_rows(_f32(t["q"][rows3, h]), _f32(t["k"][:, h]), _f32(t["v"][:, h]), rows3, scale,
+                                   key_block=S)
+    assert_close_o(o[rows3, h].float(), ro, "1M unblocked O")
+    assert_close_o(lse[h, rows3], rl, "1M unblocked LSE")
 
 
 def test_million_backward_sampled(million):
